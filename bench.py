@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark: FP32 GEMM C = A·B on one MI355X through the C ABI.
+
+A step is one product over the workload (default: M = N = K = 4096,
+row-major, A and B uniform on [-1, 1) from seed 2) with A, B and C resident in
+HBM.  W untimed steps, then K timed steps bracketed by device
+synchronisation; each launch is also bracketed by HIP events on the stream it
+is enqueued on.  Prints one JSON line.
+
+  value            2MNK * K / wall time of the K steps, TFLOP/s
+  roofline         the GEMM kernel against the FP32 matrix peak (157.3
+                   TFLOP/s): achieved = 2MNK / mean event-timed launch
+  roofline.traffic HBM bytes per launch from the rocprofv3 FETCH_SIZE and
+                   WRITE_SIZE counters recorded under profiles/, each scaled
+                   by the factor a plain copy of known size gives, or null
+                   when the kernel sources changed since they were taken
+  cpu_baseline     the CPU oracle on a bounded row sample of the same product
+
+``--copy-calibration`` instead runs a device-to-device copy of known size (for
+the counter scale factors) and prints its size.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM TFLOP/s at M=N=K=4096 fp32 (1 GPU) and % of MI355X FP32 peak"
+PEAK_FP32_TFLOPS = 157.3     # 256 CU x 2.4 GHz x 256 FP32 flop/clk (dense)
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "4096cube": (4096, 4096, 4096, "uniform", 2),
+    "256cube": (256, 256, 256, "uniform", 1),
+    "ragged": (1000, 1500, 777, "uniform", 3),
+    "skinny": (65536, 128, 256, "normal", 4),
+    "8192cube": (8192, 8192, 8192, "normal", 5),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.txt")
+
+
+def kernel_source_hash() -> str:
+    from tiled_fp32_gemm_amd import build
+    h = hashlib.sha256()
+    for p in build.sources():
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, src_hash: str):
+    """Calibrated HBM bytes per launch from profiles/, if still current."""
+    path = TRAFFIC_FILE.format(kernel=kernel, workload=workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_hash") != src_hash or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(A, B, M, N, K, rows: int) -> dict:
+    import oracle
+    rows = min(rows, M)
+    sub = A[:rows]
+    oracle.gemm(sub[:8], B, with_t=False)           # load + warm the library
+    t0 = time.perf_counter()
+    oracle.gemm(sub, B, with_t=False)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6),
+            "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product "
+                      f"(C only, fp64 accumulation), {dt:.2f} s"}
+
+
+def copy_calibration(nbytes: int) -> None:
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    src.uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="4096cube", choices=sorted(WORKLOADS))
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "simple"])
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of the product the CPU oracle computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs "
+              "the kernel on one GPU only (one GPU's share of a sharded "
+              "product is the same kernel at a smaller shape)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import seedgen
+    import tiled_fp32_gemm_amd as sg
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sg.load()   # raises if the HIP library is missing: there is no fallback
+
+    M, N, K, dist, seed = WORKLOADS[args.workload]
+    A, B = seedgen.gemm_inputs(M, N, K, dist, seed)
+    dev = torch.device("cuda:0")
+    tA = torch.from_numpy(A).to(dev)
+    tB = torch.from_numpy(B).to(dev)
+    tC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    algo = sg.ALGOS[args.algo]
+    plan = sg.plan(tA, tB, tC, algo)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step():
+        st = sg.sgemm_ex(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
+                         tC.data_ptr(), N, sh, algo)
+        if st != sg.OK:
+            raise sg.SgemmError(st, "sgemm_ex")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    flops = 2.0 * M * N * K
+    value = flops * args.steps / wall / 1e12
+    kern_s = float(ev_ms.mean()) / 1e3
+    achieved = flops / kern_s / 1e12
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(plan["kernel"], args.workload, src_hash)
+    compulsory = 4.0 * (M * K + K * N + M * N)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"sgemm {args.workload}: C=A·B, M={M} N={N} K={K}, "
+                        f"row-major fp32, A,B {dist} seed {seed}",
+            "M": M, "N": N, "K": K, "algo": args.algo,
+            "kernel": plan["kernel"], "tile": [plan["tile_m"], plan["tile_n"],
+                                                plan["tile_k"]],
+            "workgroups": plan["workgroups"],
+            "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
+            "compulsory_hbm_gbs": round(compulsory / kern_s / 1e9, 1),
+            "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+            "kernel_ms_p10_p90": [round(float(np.percentile(ev_ms, 10)), 5),
+                                  round(float(np.percentile(ev_ms, 90)), 5)],
+            "source_hash": src_hash,
+            "device": torch.cuda.get_device_name(dev),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,141 @@
+/*
+ * sgemm.h -- single-precision matrix product C = A·B on an AMD Instinct
+ * MI355X (gfx950), row-major, behind a plain C ABI.
+ *
+ * The operation.  For 0 <= i < M and 0 <= j < N
+ *
+ *      C[i*ldc + j] = sum_{k=0}^{K-1} A[i*lda + k] * B[k*ldb + j]
+ *
+ * This is the textbook product that the tiled kernels of the pages reach by
+ * other data movement only: tiling, shared-memory layout, vectorised loads and
+ * register tiles change where data travels, not the result ("CUDA in depth
+ * (5): vectorized load and shared-memory layout", section on the GEMM data
+ * path).  Row-major storage with leading dimensions that set where each row
+ * begins, possibly wider than the logical row, is the convention of the same
+ * page's section on leading dimensions.  There is no alpha or beta: C is
+ * overwritten.  Summation order is the kernel's own; results are
+ * run-to-run deterministic (no atomics, no split-K races) and agree with the
+ * exact sum within 1e-5 * sum_k |A[i][k]| |B[k][j]| for finite inputs.
+ *
+ * Arguments common to every entry point.
+ *   M, N, K   logical sizes; C is M x N, A is M x K, B is K x N.  >= 0.
+ *   A, lda    device pointer to A[0][0]; row i starts at A + i*lda.
+ *             lda >= max(1, K).  Columns K..lda-1 are never read.
+ *   B, ldb    device pointer to B[0][0]; row k starts at B + k*ldb.
+ *             ldb >= max(1, N).  Columns N..ldb-1 are never read.
+ *   C, ldc    device pointer to C[0][0]; row i starts at C + i*ldc.
+ *             ldc >= max(1, N).  Columns N..ldc-1 are never written.
+ *   stream    HIP stream the kernels are enqueued on (0 = null stream).
+ *
+ * Ownership and ordering.  All three matrices are device memory owned by the
+ * caller; the library neither allocates, frees nor retains them.  Calls return
+ * once the work is enqueued, without synchronising: the buffers must stay
+ * valid until the stream has passed the call.  C must not overlap A or B (the
+ * same no-overlap contract the pages state for their tiled transpose kernel,
+ * "Memory-bank mechanism and accelerated compute", section on the transpose
+ * kernel).  Pointers must be 4-byte aligned; any alignment and any leading
+ * dimension are accepted, and the 128-bit load path is chosen internally when
+ * the pointer is 16-byte aligned and the leading dimension and row length are
+ * multiples of 4 (same pages, sections on contiguity and alignment and on
+ * leading dimensions).
+ *
+ * Errors.  Arguments are checked before any HIP call; a rejected call
+ * enqueues nothing and leaves C untouched.
+ *   SGEMM_ERR_INVALID_ARG  negative size; leading dimension too small; a
+ *                          null or misaligned (not 4-byte) pointer for a
+ *                          non-empty operand; C overlapping A or B; an
+ *                          unknown algo.
+ *   SGEMM_ERR_UNSUPPORTED  an operand spans 2 GiB or more (the kernels
+ *                          address each operand with 32-bit byte offsets).
+ *   SGEMM_ERR_LAUNCH       the HIP launch reported an error.
+ * M == 0 or N == 0 returns SGEMM_OK with nothing enqueued; K == 0 writes
+ * C = 0 (the empty sum).
+ *
+ * Thread safety.  Stateless and reentrant; concurrent calls on different
+ * streams are independent.
+ */
+#ifndef SGEMM_H
+#define SGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+/* The HIP stream handle type, identical to the one hip_runtime_api.h
+ * declares (a repeated identical typedef is valid C11 and C++). */
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_VERSION 100 /* 1.0.0 */
+
+/* Status codes. */
+#define SGEMM_OK 0
+#define SGEMM_ERR_INVALID_ARG 1
+#define SGEMM_ERR_UNSUPPORTED 2
+#define SGEMM_ERR_LAUNCH 3
+
+/* Kernel families (sgemm_ex).
+ *   AUTO    the fastest family for the shape (today: MFMA).
+ *   SIMPLE  one output per thread from 16x16 shared tiles, the basic tiled
+ *           inner loop of "CUDA in depth (4): accessing shared memory
+ *           efficiently", section on too many shared-memory reads.
+ *   FMA     8x8 register tile per thread with vector FMA instructions, the
+ *           register tiling of the same page (sections on register tiling and
+ *           on going from 1x1 to 2x2), double-buffered, 128-bit loads.
+ *   MFMA    the same staging feeding the gfx950 FP32 matrix instruction
+ *           (32x32x2, fused multiply-add in FP32, round to nearest even). */
+#define SGEMM_ALGO_AUTO 0
+#define SGEMM_ALGO_SIMPLE 1
+#define SGEMM_ALGO_FMA 2
+#define SGEMM_ALGO_MFMA 3
+
+/* C = A·B with the AUTO kernel family.  See the top of this file for the
+ * arguments, layout, ownership and errors.  Returns a status code. */
+int sgemm(int64_t M, int64_t N, int64_t K,
+          const float *A, int64_t lda,
+          const float *B, int64_t ldb,
+          float *C, int64_t ldc,
+          hipStream_t stream);
+
+/* As sgemm(), with the kernel family named by algo (SGEMM_ALGO_*); an unknown
+ * algo is SGEMM_ERR_INVALID_ARG.  Every family computes the same product. */
+int sgemm_ex(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             hipStream_t stream, int algo);
+
+/* What a call with these arguments would launch, without launching it.  The
+ * checks and return codes are those of sgemm_ex; on SGEMM_OK *plan is filled
+ * (kernel name, workgroup tile, grid).  plan must not be NULL. */
+typedef struct sgemm_plan {
+    int algo;            /* family actually used (AUTO resolved) */
+    int tile_m, tile_n;  /* C tile per workgroup */
+    int tile_k;          /* K slab staged through LDS per step */
+    int threads;         /* threads per workgroup */
+    int vec_a, vec_b;    /* 1 if A / B rows take 128-bit loads */
+    int64_t workgroups;  /* grid size (0 when nothing is launched) */
+    int lds_bytes;       /* LDS per workgroup */
+    char kernel[64];     /* kernel name, NUL-terminated */
+} sgemm_plan;
+
+int sgemm_plan_query(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     const float *C, int64_t ldc,
+                     int algo, sgemm_plan *plan);
+
+/* Static English text for a status code (never NULL). */
+const char *sgemm_status_string(int status);
+
+/* SGEMM_VERSION of the built library. */
+int sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_H */

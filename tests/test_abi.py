@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports what the header
+declares, and rejects bad arguments before any HIP call (CPU only)."""
+from __future__ import annotations
+
+import os
+import re
+
+import pytest
+
+import tiled_fp32_gemm_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+BIG = 1 << 33  # a plausible, 16-byte aligned fake device address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tiled_fp32_gemm_amd import build
+    build.ensure_built()
+    return sg.load()
+
+
+def header_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_binding_names():
+    assert sorted(header_functions()) == sorted(sg.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_one_hip_runtime_is_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    paths = set(re.findall(r"(\S*libamdhip64\.so\S*)", maps))
+    assert len(paths) == 1, paths
+
+
+def test_version_and_status_strings(lib):
+    assert sg.sgemm_version() == 100
+    assert sg.sgemm_status_string(sg.OK) == "success"
+    for st in (sg.ERR_INVALID_ARG, sg.ERR_UNSUPPORTED, sg.ERR_LAUNCH):
+        assert sg.sgemm_status_string(st) not in ("", "success")
+    assert sg.sgemm_status_string(12345) == "unknown status"
+
+
+def call(M, N, K, A=BIG, lda=None, B=BIG + (1 << 31), ldb=None,
+         C=BIG + (1 << 32), ldc=None, algo=0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    st, plan = sg.sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, algo)
+    return st, plan
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1, N=4, K=4), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=-1, K=4), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=-1), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=8, lda=7), sg.ERR_INVALID_ARG),       # lda < K
+    (dict(M=4, N=8, K=4, ldb=7), sg.ERR_INVALID_ARG),       # ldb < N
+    (dict(M=4, N=8, K=4, ldc=7), sg.ERR_INVALID_ARG),       # ldc < N
+    (dict(M=4, N=4, K=4, lda=0), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, A=0), sg.ERR_INVALID_ARG),         # null A
+    (dict(M=4, N=4, K=4, B=0), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, C=0), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, A=BIG + 2), sg.ERR_INVALID_ARG),   # not 4-byte aligned
+    (dict(M=4, N=4, K=4, C=BIG + 1), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, C=BIG + 16), sg.ERR_INVALID_ARG),  # C overlaps A
+    (dict(M=4, N=4, K=4, B=BIG + (1 << 32) + 60), sg.ERR_INVALID_ARG),  # B overlaps C
+    (dict(M=4, N=4, K=4, algo=4), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, algo=-1), sg.ERR_INVALID_ARG),
+    (dict(M=1 << 15, N=4, K=1 << 14), sg.ERR_UNSUPPORTED),  # A spans 2 GiB
+    (dict(M=(1 << 31) // 4096 + 1, N=1024, K=4, ldc=1024), sg.ERR_UNSUPPORTED),
+])
+def test_rejected_before_any_hip_call(lib, args, status):
+    st, _ = call(**args)
+    assert st == status
+    # the launching entry points apply the same checks and launch nothing
+    M, N, K = args["M"], args["N"], args["K"]
+    a = dict(A=BIG, B=BIG + (1 << 31), C=BIG + (1 << 32))
+    a.update({k: v for k, v in args.items() if k in ("A", "B", "C")})
+    lda = args.get("lda", max(K, 1))
+    ldb = args.get("ldb", max(N, 1))
+    ldc = args.get("ldc", max(N, 1))
+    assert sg.sgemm_ex(M, N, K, a["A"], lda, a["B"], ldb, a["C"], ldc, 0,
+                       args.get("algo", 0)) == status
+    if "algo" not in args:
+        assert sg.sgemm(M, N, K, a["A"], lda, a["B"], ldb, a["C"], ldc, 0) == status
+
+
+def test_empty_problems_are_noops(lib):
+    # nothing is touched when M or N is 0, so the pointers may be null
+    assert sg.sgemm(0, 5, 5, 0, 5, 0, 5, 0, 5, 0) == sg.OK
+    assert sg.sgemm(5, 0, 5, 0, 5, 0, 1, 0, 1, 0) == sg.OK
+    st, plan = call(0, 8, 8)
+    assert st == sg.OK and plan.workgroups == 0
+
+
+def test_k_zero_plans_a_zero_fill(lib):
+    st, plan = call(100, 70, 0, A=0, B=0)
+    assert st == sg.OK and plan.workgroups > 0
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,aoff,kernel,wgs", [
+    (4096, 4096, 4096, 4096, 4096, 0, "mfma_128x128x16_vavb", 1024),
+    (8192, 8192, 8192, 8192, 8192, 0, "mfma_128x128x16_vavb", 4096),
+    (65536, 128, 256, 256, 128, 0, "mfma_128x128x16_vavb", 512),
+    (1000, 1500, 777, 777, 1500, 0, "mfma_64x64x16_savb", 384),
+    (256, 256, 256, 256, 256, 0, "mfma_64x64x16_vavb", 16),
+    (256, 256, 256, 256, 256, 4, "mfma_64x64x16_savb", 16),   # A 4B-aligned only
+    (256, 256, 256, 258, 256, 0, "mfma_64x64x16_savb", 16),   # lda % 4 != 0
+])
+def test_plans(lib, M, N, K, lda, ldb, aoff, kernel, wgs):
+    st, plan = call(M, N, K, A=BIG + aoff, lda=lda, ldb=ldb,
+                    B=BIG + (1 << 31), C=BIG + (1 << 32))
+    assert st == sg.OK
+    assert plan.kernel.decode() == kernel and plan.workgroups == wgs
+    assert plan.algo == sg.ALGOS["mfma"]
+
+
+def test_plans_per_family(lib):
+    for name, prefix in (("simple", "simple_"), ("fma", "fma_"), ("mfma", "mfma_")):
+        st, plan = call(300, 200, 100, algo=sg.ALGOS[name])
+        assert st == sg.OK and plan.kernel.decode().startswith(prefix)
+        assert plan.lds_bytes <= 160 * 1024

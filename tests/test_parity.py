@@ -1,0 +1,247 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs, |C - Cref| <= 1e-5 * (|A|·|B|) elementwise
+(bit-exact where every partial sum is an integer)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import seedgen
+
+from gpu_util import DevMat, assert_close, run, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ALGOS = ["auto", "mfma", "fma", "simple"]
+
+# The five workloads: (name, M, N, K, lda, ldb, ldc, distribution, seed).
+CONFIGS = {
+    "256cube": (256, 256, 256, 256, 256, 256, "uniform", 1),
+    "4096cube": (4096, 4096, 4096, 4096, 4096, 4096, "uniform", 2),
+    "ragged": (1000, 1500, 777, 777, 1500, 1500, "uniform", 3),
+    "skinny": (65536, 128, 256, 256, 128, 128, "normal", 4),
+    "8192cube": (8192, 8192, 8192, 8192, 8192, 8192, "normal", 5),
+}
+
+_inputs: dict = {}
+
+
+def config_inputs(name):
+    if name not in _inputs:
+        M, N, K, lda, ldb, ldc, dist, seed = CONFIGS[name]
+        say(f"[inputs] {name}: M={M} N={N} K={K} {dist} seed={seed}")
+        A, B = seedgen.gemm_inputs(M, N, K, dist, seed, lda=lda, ldb=ldb)
+        _inputs[name] = (A, B, DevMat(A), DevMat(B))
+    return _inputs[name]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cleanup():
+    yield
+    _inputs.clear()
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", ["256cube", "ragged", "skinny"])
+def test_config_full(name, algo):
+    M, N, K, lda, ldb, ldc, dist, seed = CONFIGS[name]
+    A, B, dA, dB = config_inputs(name)
+    dC = DevMat(np.full((M, ldc), np.nan, np.float32))
+    say(f"[gpu] {name} algo={algo}")
+    run(M, N, K, dA, dB, dC, algo)
+    Cref, T = oracle.gemm(A[:, :K], B[:, :N], M=M, N=N, K=K)
+    err = assert_close(dC.host()[:, :N], Cref, T, f"{name}/{algo}")
+    say(f"  max normalised error {err:.3e}")
+
+
+def sample_indices(n: int, count: int, tile: int, seed: int) -> np.ndarray:
+    """First, last, tile-boundary and seeded random indices in [0, n)."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, n - 1, n - 2] + [t for b in range(tile, n, tile * 7)
+                                     for t in (b - 1, b)]
+    rand = rng.choice(n, size=count, replace=False)
+    return np.unique(np.clip(np.array(fixed + list(rand)), 0, n - 1))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", ["4096cube", "8192cube"])
+def test_config_sampled(name, algo):
+    """Full-size shapes: the GPU computes all of C; the oracle computes every
+    element of sampled rows and of sampled columns."""
+    M, N, K, lda, ldb, ldc, dist, seed = CONFIGS[name]
+    A, B, dA, dB = config_inputs(name)
+    dC = DevMat(np.full((M, ldc), np.nan, np.float32))
+    say(f"[gpu] {name} algo={algo}")
+    run(M, N, K, dA, dB, dC, algo)
+    C = dC.host()
+    assert np.all(np.isfinite(C[:, :N])), "unwritten or non-finite outputs"
+    nsamp = 48 if M <= 4096 else 24
+    rows = sample_indices(M, nsamp, 128, seed)
+    cols = sample_indices(N, nsamp, 128, seed + 100)
+    Cr, Tr = oracle.gemm(np.ascontiguousarray(A[rows, :K]), B[:, :N],
+                         M=len(rows), N=N, K=K)
+    assert_close(C[rows, :N], Cr, Tr, f"{name}/{algo} rows")
+    Cc, Tc = oracle.gemm(A[:, :K], np.ascontiguousarray(B[:K, cols]),
+                         M=M, N=len(cols), K=K)
+    err = assert_close(C[:, cols], Cc, Tc, f"{name}/{algo} cols")
+    say(f"  max normalised error (sampled) {err:.3e}")
+
+
+SWEEP = [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128,
+         129, 255, 256, 257]
+
+
+def int_case(M, N, K, seed, lda=None, ldb=None):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    A = np.full((M, lda), np.nan, np.float32)
+    B = np.full((K, ldb), np.nan, np.float32)
+    A[:, :K] = seedgen.integer_matrix(M, K, -8, 8, seed)
+    B[:, :N] = seedgen.integer_matrix(K, N, -8, 8, seed, start=M * K)
+    return A, B
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_integer_shapes_bitexact(algo):
+    """Integer data: every partial sum is an integer below 2**24, so any
+    summation order gives the same float32 bits as the rounded oracle."""
+    rng = np.random.default_rng(7)
+    shapes = [(m, n, k) for m in SWEEP for n in SWEEP for k in SWEEP]
+    picks = [shapes[i] for i in rng.choice(len(shapes), 60, replace=False)]
+    picks += [(1, 1, 1), (257, 257, 257), (1, 257, 3), (129, 1, 64),
+              (1000, 1500, 777), (300, 500, 0)]
+    for idx, (M, N, K) in enumerate(picks):
+        A, B = int_case(M, N, K, 500 + idx)
+        dA, dB = DevMat(A), DevMat(B)
+        dC = DevMat(np.full((M, N), np.nan, np.float32))
+        say(f"[gpu] int {algo} M={M} N={N} K={K}")
+        run(M, N, K, dA, dB, dC, algo)
+        Cref, _ = oracle.gemm(A[:, :K], B[:, :N], M=M, N=N, K=K, with_t=False)
+        got = dC.host()
+        assert np.array_equal(got, Cref.astype(np.float32)), (algo, M, N, K)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("offs", [(0, 0, 0), (1, 2, 3), (3, 1, 2), (2, 3, 1)])
+def test_leading_dims_offsets_and_sentinels(algo, offs):
+    """Leading dimensions wider than the rows (odd and multiple-of-4 ones),
+    base addresses that are only 4-byte aligned, NaN in every A and B gap and
+    sentinels in C's gaps, which must survive untouched."""
+    for (M, N, K, lda, ldb, ldc) in [(130, 150, 77, 80, 151, 157),
+                                     (200, 136, 96, 100, 140, 144),
+                                     (65, 257, 33, 36, 260, 259)]:
+        A, B = seedgen.gemm_inputs(M, N, K, "uniform", 900 + M, lda=lda,
+                                   ldb=ldb, fill=np.nan)
+        dA = DevMat(A, off=offs[0], pad=np.nan)
+        dB = DevMat(B, off=offs[1], pad=np.nan)
+        C0 = np.full((M, ldc), -123.5, np.float32)
+        dC = DevMat(C0, off=offs[2], pad=-77.0)
+        say(f"[gpu] ld {algo} offs={offs} M={M} N={N} K={K} ld={lda},{ldb},{ldc}")
+        run(M, N, K, dA, dB, dC, algo)
+        got = dC.host()
+        Cref, T = oracle.gemm(A[:, :K], B[:, :N], M=M, N=N, K=K)
+        assert_close(got[:, :N], Cref, T, f"ld {algo} {offs}")
+        assert np.all(got[:, N:] == -123.5), "C padding columns were written"
+        w = dC.whole()
+        assert np.all(w[:offs[2]] == -77.0)
+        assert np.all(w[offs[2] + M * ldc:] == -77.0), "wrote past C"
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_deterministic_and_stream_independent(algo):
+    M, N, K = 777, 555, 333
+    A, B = seedgen.gemm_inputs(M, N, K, "normal", 77)
+    dA, dB = DevMat(A), DevMat(B)
+    outs = []
+    s = torch.cuda.Stream()
+    for stream in (None, None, s):
+        dC = DevMat(np.zeros((M, N), np.float32))
+        say(f"[gpu] determinism {algo} stream={'side' if stream else 'current'}")
+        if stream is not None:
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                run(M, N, K, dA, dB, dC, algo, stream=stream)
+        else:
+            run(M, N, K, dA, dB, dC, algo)
+        outs.append(dC.host().copy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_power_of_two_scaling_is_exact(algo):
+    M, N, K = 300, 260, 190
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 88)
+    dB = DevMat(B)
+    res = []
+    for scale in (1.0, 2.0, 0.25):
+        dA = DevMat((A * np.float32(scale)).astype(np.float32))
+        dC = DevMat(np.zeros((M, N), np.float32))
+        say(f"[gpu] scaling {algo} x{scale}")
+        run(M, N, K, dA, dB, dC, algo)
+        res.append(dC.host().copy())
+    assert np.array_equal(res[1], 2.0 * res[0])
+    assert np.array_equal(res[2], 0.25 * res[0])
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_k_zero_writes_zeros_and_empty_is_noop(algo):
+    import tiled_fp32_gemm_amd as sg
+    M, N = 70, 90
+    dC = DevMat(np.full((M, N), 5.0, np.float32))
+    say(f"[gpu] K=0 {algo}")
+    st = sg.sgemm_ex(M, N, 0, 0, 1, 0, N, dC.ptr, N,
+                     torch.cuda.current_stream().cuda_stream, sg.ALGOS[algo])
+    assert st == sg.OK
+    torch.cuda.synchronize()
+    assert np.all(dC.host() == 0.0)
+    dC2 = DevMat(np.full((4, 4), 5.0, np.float32))
+    assert sg.sgemm_ex(0, 4, 4, 0, 4, 0, 4, dC2.ptr, 4, 0, sg.ALGOS[algo]) == sg.OK
+    torch.cuda.synchronize()
+    assert np.all(dC2.host() == 5.0)
+
+
+def test_largest_operand(algo="auto"):
+    """A just under the 2 GiB operand limit (integer data made on the GPU);
+    sampled rows, including the last, against the oracle, bit-exact."""
+    M, K, N = 32768, 16383, 64
+    say(f"[gpu] largest operand: A {M}x{K} ({M * K * 4 / 2**30:.4f} GiB)")
+    i = torch.arange(M, device="cuda:0", dtype=torch.int64)[:, None]
+    k = torch.arange(K, device="cuda:0", dtype=torch.int64)[None, :]
+    dA = ((i * 7 + k * 3) % 17 - 8).to(torch.float32).contiguous()
+    B = seedgen.integer_matrix(K, N, -8, 8, 4242)
+    dB = torch.from_numpy(B).to("cuda:0")
+    dC = torch.full((M, N), float("nan"), device="cuda:0")
+    import tiled_fp32_gemm_amd as sg
+    st = sg.sgemm(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+                  torch.cuda.current_stream().cuda_stream)
+    assert st == sg.OK
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4095, 4096, 20000, M - 2, M - 1])
+    Arows = dA[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
+    Cref, _ = oracle.gemm(Arows, B, with_t=False)
+    got = dC[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
+    assert np.array_equal(got, Cref.astype(np.float32))
+    assert bool(torch.isfinite(dC).all())
+    del dA, dC
+
+
+def test_matmul_wrapper_on_views():
+    """The tensor convenience: row-stride views and the current stream."""
+    import tiled_fp32_gemm_amd as sg
+    M, N, K = 123, 77, 45
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 99)
+    big = torch.full((M, K + 11), float("nan"), device="cuda:0")
+    big[:, :K] = torch.from_numpy(A)
+    tA = big[:, :K]
+    tB = torch.from_numpy(B).to("cuda:0")
+    say("[gpu] matmul wrapper")
+    out = sg.matmul(tA, tB)
+    torch.cuda.synchronize()
+    Cref, T = oracle.gemm(A, B)
+    assert_close(out.cpu().numpy(), Cref, T, "matmul")
+    with pytest.raises(ValueError):
+        sg.matmul(tA.double(), tB)
+    with pytest.raises(ValueError):
+        sg.matmul(tA.t(), tB)

@@ -1,0 +1,88 @@
+// common.hpp -- device helpers shared by the gfx950 SGEMM kernels.
+//
+// Buffer resources.  Every operand is read and written through a raw buffer
+// resource (base, byte size).  A lane whose element lies outside the logical
+// matrix is given the byte offset kOob, which is past the end of any resource
+// the host accepts (operands are < 2 GiB), so its load returns 0 and its store
+// is dropped by the hardware range check.  That is the pages' predicated edge
+// load that writes 0 for invalid elements ("CUDA in depth (5)", section on
+// edges), without a branch, and no stale value is ever multiplied by 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a gfx9-family buffer descriptor: 32-bit data format, raw (no
+// swizzle, stride 0) addressing.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                          uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ f32x4 load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                       float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off,
+                                        0, 0);
+}
+
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                       f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off,
+                                         0, 0);
+}
+
+// Kernel arguments, identical for every family.  Sizes are checked on the host
+// (M, N, K >= 0, every operand < 2 GiB), so 32-bit byte offsets suffice.
+struct GemmArgs {
+  const float* A;
+  const float* B;
+  float* C;
+  uint32_t a_bytes, b_bytes, c_bytes;  // resource sizes
+  int M, N, K;
+  int lda, ldb, ldc;
+  int tiles_m, tiles_n;                // C tiles along M and N
+  int group_m;                         // tile rows per ordering group
+};
+
+// Workgroup -> C tile.  Workgroups are handed to the 8 XCDs round-robin
+// (workgroup w runs on XCD w % 8), and each XCD has its own L2.  The id is
+// first renumbered so that ids running on one XCD are consecutive, then
+// consecutive ids walk a group of group_m tile rows column by column, so the
+// tiles one XCD holds at a time share A row panels and B column panels.
+__device__ __forceinline__ void tile_of_workgroup(const GemmArgs& g, int& tm,
+                                                  int& tn) {
+  const int nwg = g.tiles_m * g.tiles_n;
+  const int w = (int)blockIdx.x;
+  const int q = nwg >> 3, rem = nwg & 7;
+  const int xcd = w & 7, local = w >> 3;
+  const int L = xcd * q + (xcd < rem ? xcd : rem) + local;
+  const int per_group = g.group_m * g.tiles_n;
+  const int grp = L / per_group;
+  const int first_m = grp * g.group_m;
+  const int rows = min(g.tiles_m - first_m, g.group_m);
+  const int in_grp = L - grp * per_group;
+  tm = first_m + in_grp % rows;
+  tn = in_grp / rows;
+}
+
+}  // namespace sg
