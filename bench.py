@@ -103,7 +103,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="4096cube", choices=sorted(WORKLOADS))
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "simple"])
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the product the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
