@@ -46,7 +46,9 @@
  *                          non-empty operand; C overlapping A or B; an
  *                          unknown algo.
  *   SGEMM_ERR_UNSUPPORTED  an operand spans 2 GiB or more (the kernels
- *                          address each operand with 32-bit byte offsets).
+ *                          address each operand with 32-bit byte offsets),
+ *                          or SGEMM_ALGO_MFMA_DIRECT was asked for rows
+ *                          that do not allow 128-bit loads.
  *   SGEMM_ERR_LAUNCH       the HIP launch reported an error.
  * M == 0 or N == 0 returns SGEMM_OK with nothing enqueued; K == 0 writes
  * C = 0 (the empty sum).
@@ -78,19 +80,28 @@ extern "C" {
 #define SGEMM_ERR_LAUNCH 3
 
 /* Kernel families (sgemm_ex).
- *   AUTO    the fastest family for the shape (today: MFMA).
+ *   AUTO    the fastest family for the arguments: MFMA_DIRECT when A and B
+ *           rows allow 128-bit loads, else MFMA; the tile size follows the
+ *           shape.
  *   SIMPLE  one output per thread from 16x16 shared tiles, the basic tiled
  *           inner loop of "CUDA in depth (4): accessing shared memory
  *           efficiently", section on too many shared-memory reads.
  *   FMA     8x8 register tile per thread with vector FMA instructions, the
  *           register tiling of the same page (sections on register tiling and
  *           on going from 1x1 to 2x2), double-buffered, 128-bit loads.
- *   MFMA    the same staging feeding the gfx950 FP32 matrix instruction
- *           (32x32x2, fused multiply-add in FP32, round to nearest even). */
+ *   MFMA    the same register staging feeding the gfx950 FP32 matrix
+ *           instruction (32x32x2, fused multiply-add in FP32, round to
+ *           nearest even); any alignment.
+ *   MFMA_DIRECT  the same matrix instructions with slabs loaded from global
+ *           memory straight into LDS (three LDS stages); needs A and B
+ *           16-byte aligned with lda, K, ldb and N multiples of 4
+ *           ("CUDA in depth (5)", section on contiguity and alignment),
+ *           else SGEMM_ERR_UNSUPPORTED.  Bitwise equal to MFMA. */
 #define SGEMM_ALGO_AUTO 0
 #define SGEMM_ALGO_SIMPLE 1
 #define SGEMM_ALGO_FMA 2
 #define SGEMM_ALGO_MFMA 3
+#define SGEMM_ALGO_MFMA_DIRECT 4
 
 /* C = A·B with the AUTO kernel family.  See the top of this file for the
  * arguments, layout, ownership and errors.  Returns a status code. */

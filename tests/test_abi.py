@@ -75,7 +75,10 @@ def call(M, N, K, A=BIG, lda=None, B=BIG + (1 << 31), ldb=None,
     (dict(M=4, N=4, K=4, C=BIG + 1), sg.ERR_INVALID_ARG),
     (dict(M=4, N=4, K=4, C=BIG + 16), sg.ERR_INVALID_ARG),  # C overlaps A
     (dict(M=4, N=4, K=4, B=BIG + (1 << 32) + 60), sg.ERR_INVALID_ARG),  # B overlaps C
-    (dict(M=4, N=4, K=4, algo=4), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, algo=5), sg.ERR_INVALID_ARG),
+    (dict(M=4, N=4, K=4, A=BIG + 4, algo=4), sg.ERR_UNSUPPORTED),  # direct, A not 16B
+    (dict(M=4, N=4, K=6, lda=6, algo=4), sg.ERR_UNSUPPORTED),      # direct, K % 4
+    (dict(M=4, N=6, K=4, ldb=6, ldc=6, algo=4), sg.ERR_UNSUPPORTED),  # direct, N % 4
     (dict(M=4, N=4, K=4, algo=-1), sg.ERR_INVALID_ARG),
     (dict(M=1 << 15, N=4, K=1 << 14), sg.ERR_UNSUPPORTED),  # A spans 2 GiB
     (dict(M=(1 << 31) // 4096 + 1, N=1024, K=4, ldc=1024), sg.ERR_UNSUPPORTED),
@@ -104,30 +107,39 @@ def test_empty_problems_are_noops(lib):
     assert st == sg.OK and plan.workgroups == 0
 
 
-def test_k_zero_plans_a_zero_fill(lib):
-    st, plan = call(100, 70, 0, A=0, B=0)
-    assert st == sg.OK and plan.workgroups > 0
+@pytest.mark.parametrize("algo", sorted(sg.ALGOS))
+def test_k_zero_plans_a_zero_fill(lib, algo):
+    # neither A nor B is read, so null, unaligned or narrow ones are fine
+    for a, lda in ((0, 1), (BIG + 4, 3)):
+        st, plan = call(100, 70, 0, A=a, lda=lda, B=0, algo=sg.ALGOS[algo])
+        assert st == sg.OK and plan.workgroups > 0 and plan.kernel
 
 
 @pytest.mark.parametrize("M,N,K,lda,ldb,aoff,kernel,wgs", [
-    (4096, 4096, 4096, 4096, 4096, 0, "mfma_128x128x16_vavb", 1024),
-    (8192, 8192, 8192, 8192, 8192, 0, "mfma_128x128x16_vavb", 4096),
-    (65536, 128, 256, 256, 128, 0, "mfma_128x128x16_vavb", 512),
+    (4096, 4096, 4096, 4096, 4096, 0, "mfma_lds_256x256x16_vavb", 256),
+    (8192, 8192, 8192, 8192, 8192, 0, "mfma_lds_256x256x16_vavb", 1024),
+    (65536, 128, 256, 256, 128, 0, "mfma_lds_128x128x16_vavb", 512),
     (1000, 1500, 777, 777, 1500, 0, "mfma_64x64x16_savb", 384),
-    (256, 256, 256, 256, 256, 0, "mfma_64x64x16_vavb", 16),
-    (256, 256, 256, 256, 256, 4, "mfma_64x64x16_savb", 16),   # A 4B-aligned only
-    (256, 256, 256, 258, 256, 0, "mfma_64x64x16_savb", 16),   # lda % 4 != 0
+    (256, 256, 256, 256, 256, 0, "mfma_lds_64x64x16_vavb", 16),
+    (256, 256, 256, 256, 256, 4, "mfma_64x64x16_savb", 16),    # A 4B-aligned only
+    (256, 256, 256, 258, 256, 0, "mfma_64x64x16_savb", 16),    # lda % 4 != 0
+    (4096, 4096, 4095, 4095, 4096, 0, "mfma_256x128x16_savb", 512),
+    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x16_vavb", 2209),
+    (2048, 2048, 2048, 2048, 2048, 0, "mfma_lds_128x128x16_vavb", 256),
+    (4100, 4100, 4096, 4096, 4100, 0, "mfma_lds_64x64x16_vavb", 4225),
 ])
 def test_plans(lib, M, N, K, lda, ldb, aoff, kernel, wgs):
     st, plan = call(M, N, K, A=BIG + aoff, lda=lda, ldb=ldb,
                     B=BIG + (1 << 31), C=BIG + (1 << 32))
     assert st == sg.OK
     assert plan.kernel.decode() == kernel and plan.workgroups == wgs
-    assert plan.algo == sg.ALGOS["mfma"]
+    direct = kernel.startswith("mfma_lds")
+    assert plan.algo == sg.ALGOS["mfma_direct" if direct else "mfma"]
 
 
 def test_plans_per_family(lib):
-    for name, prefix in (("simple", "simple_"), ("fma", "fma_"), ("mfma", "mfma_")):
-        st, plan = call(300, 200, 100, algo=sg.ALGOS[name])
+    for name, prefix in (("simple", "simple_"), ("fma", "fma_"), ("mfma", "mfma_"),
+                         ("mfma_direct", "mfma_lds_")):
+        st, plan = call(300, 200, 100, lda=100, algo=sg.ALGOS[name])
         assert st == sg.OK and plan.kernel.decode().startswith(prefix)
         assert plan.lds_bytes <= 160 * 1024

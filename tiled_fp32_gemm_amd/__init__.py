@@ -26,7 +26,7 @@ __all__ = ["sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_status_string",
            "ERR_LAUNCH", "EXPORTED_SYMBOLS"]
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
-ALGOS = {"auto": 0, "simple": 1, "fma": 2, "mfma": 3}
+ALGOS = {"auto": 0, "simple": 1, "fma": 2, "mfma": 3, "mfma_direct": 4}
 EXPORTED_SYMBOLS = ("sgemm", "sgemm_ex", "sgemm_plan_query",
                     "sgemm_status_string", "sgemm_version")
 

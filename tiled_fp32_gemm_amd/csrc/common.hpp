@@ -51,6 +51,15 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                          0, 0);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's data lands
+// at lds_dst + 16 l bytes (lds_dst must be the same for the whole wave);
+// out-of-range lanes write zeros.
+__device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r,
+                                             float* lds_dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_dst, 16, off, 0, 0, 0);
+}
+
 // Kernel arguments, identical for every family.  Sizes are checked on the host
 // (M, N, K >= 0, every operand < 2 GiB), so 32-bit byte offsets suffice.
 struct GemmArgs {

@@ -5,7 +5,8 @@
 // -> register fragments -> multiply-add; "CUDA in depth (5)", section on the
 // GEMM data path), mapped onto CDNA4:
 //
-//  * One workgroup owns a BM x BN tile of C and walks K in slabs of BK = 16.
+//  * One workgroup owns a BM x BN tile of C and walks K in slabs of BK (16 or
+//    32) floats.
 //    Its waves split the tile into WM x WN wave tiles, each a grid of 32 x 32
 //    blocks computed by v_mfma_f32_32x32x2_f32 (FP32 in, FP32 fused
 //    multiply-add, accumulators in registers).
@@ -16,18 +17,19 @@
 //    before the matrix instructions of slab t and written to the other LDS
 //    stage after them, with one barrier per slab.
 //  * LDS layouts, chosen for gfx950's 64 banks of 4 bytes:
-//      As[BM][20]   A rows, k contiguous (16 used, 4 pad).  A row is 80 bytes
-//                   = 5 x 16: sixteen consecutive rows start at sixteen
-//                   different 16-byte bank groups, so the 128-bit stores and
-//                   reads below, which give consecutive lanes consecutive
-//                   rows, touch each bank once per 16 lanes.
+//      As[BM][BK+4] A rows, k contiguous (BK used, 4 pad).  A row is BK + 4
+//                   floats, an odd number of 16-byte units (5 or 9): sixteen
+//                   consecutive rows start at sixteen different 16-byte bank
+//                   groups, so the 128-bit stores and reads below, which give
+//                   consecutive lanes consecutive rows, touch each bank once
+//                   per 16 lanes.
 //      Bs[16][BN+4] B rows as in memory (j contiguous).  128-bit stores are
 //                   256 contiguous bytes per 16 lanes; 32-bit reads give
 //                   lanes 0-31 one row and lanes 32-63 the row 8 below, and
 //                   8 * (BN + 4) = 32 (mod 64) puts the two halves on
 //                   disjoint banks.
-//  * The k order inside a slab is regrouped: MFMA step p (0..7) takes k = p
-//    from lanes 0-31 and k = 8 + p from lanes 32-63.  Every k of the slab is
+//  * The k order inside each 16-deep sub-slab is regrouped: MFMA step p (0..7)
+//    takes k = p from lanes 0-31 and k = 8 + p from lanes 32-63.  Every k is
 //    still used exactly once for A and B alike, and each lane's eight A values
 //    are contiguous in As, so they come in as two 128-bit reads (the pages'
 //    "segmented storage matching the register tile's read order",
@@ -42,9 +44,11 @@
 
 namespace sg {
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK_ = 16>
 struct MfmaCfg {
-  static constexpr int BK = 16;
+  static constexpr int BK = BK_;
+  static constexpr int SUB = BK / 16;  // 16-deep sub-slabs per slab
+  static constexpr int CPR = BK / 4;   // 4-float groups per A tile row
   static constexpr int WAVES_M = BM / WM;
   static constexpr int WAVES_N = BN / WN;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -64,22 +68,25 @@ struct MfmaCfg {
   static_assert(B_SLOTS * NT * 4 == BK * BN, "B tile must split evenly");
   static_assert((8 * RB) % 64 == 32, "B read halves must use disjoint banks");
   static_assert((RA / 4) % 2 == 1, "A row stride must be an odd number of 16B");
+  static_assert(BK % 16 == 0 && BK <= 64, "slabs are whole 16-deep sub-slabs");
 };
 
 // One 4-float group of the A slab: slot s of thread t covers A tile row
-// (f % 16) + 16 * (f / 64) and k = 4 * ((f / 16) % 4), f = s * NT + t, so the
-// 16 lanes of each quarter-wave hold 16 consecutive rows at one k group.
+// (f % 16) + 16 * (f / (16 * CPR)) and k = 4 * ((f / 16) % CPR),
+// f = s * NT + t, so the 16 lanes of each quarter-wave hold 16 consecutive
+// rows at one k group.
 template <class Cfg>
 __device__ __forceinline__ void a_slot(int f, int& row, int& kq) {
-  row = (f & 15) + ((f >> 6) << 4);
-  kq = (f >> 4) & 3;
+  row = (f & 15) + (f / (16 * Cfg::CPR)) * 16;
+  kq = (f >> 4) % Cfg::CPR;
 }
 
-template <int BM, int BN, int WM, int WN, bool VEC_A, bool VEC_B>
+template <int BM, int BN, int WM, int WN, int BK_, bool VEC_A, bool VEC_B>
 __global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN))
 sgemm_mfma_kernel(GemmArgs g) {
-  using Cfg = MfmaCfg<BM, BN, WM, WN>;
+  using Cfg = MfmaCfg<BM, BN, WM, WN, BK_>;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
+  constexpr int SUB = Cfg::SUB;
   constexpr int RA = Cfg::RA, RB = Cfg::RB;
 
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
@@ -188,28 +195,31 @@ sgemm_mfma_kernel(GemmArgs g) {
 
     const float* as = As + cur * Cfg::A_STAGE;
     const float* bs = Bs + cur * Cfg::B_STAGE;
-    f32x4 af[TA][2];
 #pragma unroll
-    for (int i = 0; i < TA; ++i) {
-      const float* p = as + (wm0 + 32 * i + li) * RA + 8 * lh;
-      af[i][0] = *reinterpret_cast<const f32x4*>(p);
-      af[i][1] = *reinterpret_cast<const f32x4*>(p + 4);
-    }
-    float bf[TB][8];
+    for (int u = 0; u < SUB; ++u) {
+      f32x4 af[TA][2];
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
+      for (int i = 0; i < TA; ++i) {
+        const float* p = as + (wm0 + 32 * i + li) * RA + 16 * u + 8 * lh;
+        af[i][0] = *reinterpret_cast<const f32x4*>(p);
+        af[i][1] = *reinterpret_cast<const f32x4*>(p + 4);
+      }
+      float bf[TB][8];
 #pragma unroll
-      for (int j = 0; j < TB; ++j)
-        bf[j][p] = bs[(8 * lh + p) * RB + wn0 + 32 * j + li];
-
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-#pragma unroll
-      for (int i = 0; i < TA; ++i)
+      for (int p = 0; p < 8; ++p)
 #pragma unroll
         for (int j = 0; j < TB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-              af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
+          bf[j][p] = bs[(16 * u + 8 * lh + p) * RB + wn0 + 32 * j + li];
+
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+#pragma unroll
+        for (int i = 0; i < TA; ++i)
+#pragma unroll
+          for (int j = 0; j < TB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
+    }
 
     if (more) store_slab(cur ^ 1);
     __syncthreads();

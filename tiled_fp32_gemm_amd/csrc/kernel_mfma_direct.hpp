@@ -1,0 +1,205 @@
+// kernel_mfma_direct.hpp -- FP32 MFMA GEMM with direct global->LDS staging.
+//
+// Same tiles, MFMA microkernel, k regrouping and epilogue as
+// kernel_mfma.hpp, but the slabs go from global memory straight into LDS
+// with the gfx950 buffer-load-to-LDS form (128 bits per lane), bypassing
+// registers.  That is the nearest CDNA4 counterpart of the asynchronous copy
+// the pages mention ("Memory-bank mechanism and accelerated compute", section
+// on alternatives to padding); here it removes the staging registers and the
+// LDS store instructions, and lets three LDS stages keep two slabs in flight.
+//
+// A direct load writes lane l's 16 bytes at base + 16 l, so each layout is
+// chosen as a permutation of 16-byte units that keeps every load instruction
+// lane-linear and every read conflict-free on 64 banks of 4 bytes:
+//
+//   A stage (BM x 16): rows in blocks of 16; inside a block the four k
+//     groups follow each other, row fastest: unit(r, c) = 64 (r / 16) +
+//     16 c + r % 16.  A load instruction covers 16 rows x 64 contiguous
+//     bytes of global memory; an MFMA fragment read by 16 consecutive lanes
+//     (16 consecutive rows, one k group) is 256 contiguous bytes.
+//   B stage (16 x BN): rows as in memory with the 16-byte units of rows 8..15
+//     XOR-swizzled by 8: unit(k, q) = k BN/4 + (q ^ 8 [k >= 8]).  The 32-bit
+//     reads give lanes 0-31 row p and lanes 32-63 row 8 + p; the swizzle puts
+//     the two halves on the two disjoint halves of the banks (the pages' XOR
+//     swizzle idea, "Memory-bank mechanism and accelerated compute", section
+//     on alternatives to padding, applied at 16-byte granularity so that the
+//     128-bit units stay whole).
+//
+// Out-of-range lanes read 0 into LDS (buffer range check), which gives the
+// zero-filled edges.  Pipeline: slabs t and t+1 are in flight while slab t is
+// computed; at the top of each step a wave waits until its own loads of slab
+// t have landed, then one barrier makes every wave's loads visible and frees
+// the stage of slab t-1 for slab t+2.  Requires 128-bit-capable A and B rows
+// (16-byte aligned, leading dimension and row length multiples of 4).
+#pragma once
+
+#include "common.hpp"
+
+namespace sg {
+
+template <int BM, int BN, int WM, int WN>
+struct DirectCfg {
+  static constexpr int BK = 16, STAGES = 3;
+  static constexpr int WAVES_N = BN / WN;
+  static constexpr int NT = 64 * (BM / WM) * (BN / WN);
+  static constexpr int TA = WM / 32, TB = WN / 32;
+  static constexpr int A_STAGE = BM * BK;   // floats
+  static constexpr int B_STAGE = BK * BN;
+  static constexpr int LDS_FLOATS = STAGES * (A_STAGE + B_STAGE);
+  static constexpr int A_SLOTS = BM * BK / 4 / NT;
+  static constexpr int B_SLOTS = BK * BN / 4 / NT;
+  static constexpr int LOADS = A_SLOTS + B_SLOTS;  // vector loads per slab
+  static_assert(A_SLOTS * NT * 4 == BM * BK && B_SLOTS * NT * 4 == BK * BN,
+                "slabs must split into whole 64-lane load instructions");
+  static_assert(BM % 32 == 0 && BN >= 64 && BN % 64 == 0, "tile shape");
+  static_assert(LOADS < 16, "wait count must fit the low field");
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+template <int n>
+struct VmWait {
+  static constexpr int imm = (n & 0xF) | (0x7 << 4) | (0xF << 8);
+};
+
+template <int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN))
+sgemm_mfma_direct_kernel(GemmArgs g) {
+  using Cfg = DirectCfg<BM, BN, WM, WN>;
+  constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
+  constexpr int QB = BN / 4;  // 16-byte units per B row
+
+  __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
+  float* const As = lds;                                // [STAGES][A_STAGE]
+  float* const Bs = lds + Cfg::STAGES * Cfg::A_STAGE;   // [STAGES][B_STAGE]
+
+  int tm, tn;
+  tile_of_workgroup(g, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / Cfg::WAVES_N) * WM;
+  const int wn0 = (wave % Cfg::WAVES_N) * WN;
+  const int li = lane & 31, lh = lane >> 5;
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+
+  // Unit u = s NT + 64 wave + lane of each load instruction, and the global
+  // element it takes.
+  uint32_t a_off[Cfg::A_SLOTS];
+  bool a_row_ok[Cfg::A_SLOTS];
+  int a_k[Cfg::A_SLOTS];
+#pragma unroll
+  for (int s = 0; s < Cfg::A_SLOTS; ++s) {
+    const int u = s * NT + 64 * wave + lane;
+    const int row = ((u >> 6) << 4) + (u & 15), c = (u >> 4) & 3;
+    a_row_ok[s] = (m0 + row) < g.M;
+    a_k[s] = 4 * c;
+    a_off[s] = ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u;
+  }
+  uint32_t b_off[Cfg::B_SLOTS];
+  bool b_col_ok[Cfg::B_SLOTS];
+  int b_k[Cfg::B_SLOTS];
+#pragma unroll
+  for (int s = 0; s < Cfg::B_SLOTS; ++s) {
+    const int u = s * NT + 64 * wave + lane;
+    const int k = u / QB, q = (u % QB) ^ ((k & 8) ? 8 : 0);
+    b_k[s] = k;
+    b_col_ok[s] = (n0 + 4 * q) < g.N;
+    b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u;
+  }
+
+  // Issue the direct loads of the slab starting at k0 into stage st.
+  auto issue = [&](int k0, int st) {
+#pragma unroll
+    for (int s = 0; s < Cfg::A_SLOTS; ++s) {
+      float* dst = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave);
+      const bool ok = a_row_ok[s] && (k0 + a_k[s]) < g.K;
+      load4_to_lds(ra, dst, ok ? a_off[s] + (uint32_t)k0 * 4u : kOob);
+    }
+#pragma unroll
+    for (int s = 0; s < Cfg::B_SLOTS; ++s) {
+      float* dst = Bs + st * Cfg::B_STAGE + 4 * (s * NT + 64 * wave);
+      const bool ok = b_col_ok[s] && (k0 + b_k[s]) < g.K;
+      load4_to_lds(rb, dst, ok ? b_off[s] + (uint32_t)k0 * (uint32_t)g.ldb * 4u : kOob);
+    }
+  };
+
+  f32x16 acc[TA][TB];
+#pragma unroll
+  for (int i = 0; i < TA; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nslab = (g.K + BK - 1) / BK;
+  if (nslab > 0) issue(0, 0);
+  if (nslab > 1) issue(BK, 1);
+
+  int st = 0;  // stage of slab t
+  for (int t = 0; t < nslab; ++t) {
+    if (t + 1 < nslab)
+      __builtin_amdgcn_s_waitcnt(VmWait<Cfg::LOADS>::imm);
+    else
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    // A plain workgroup barrier: the wait above already covers this wave's
+    // loads of slab t, and the "memory" clobber keeps the compiler from
+    // moving LDS accesses across it.  (A full __syncthreads() fence would
+    // also wait for slab t+1, which must stay in flight.)
+    asm volatile("s_barrier" ::: "memory");
+    if (t + 2 < nslab) issue((t + 2) * BK, st == 0 ? 2 : st - 1);
+
+    const float* as = As + st * Cfg::A_STAGE;
+    const float* bs = Bs + st * Cfg::B_STAGE;
+    f32x4 af[TA][2];
+#pragma unroll
+    for (int i = 0; i < TA; ++i) {
+      const int row = wm0 + 32 * i + li;
+      const float* p = as + 4 * (((row >> 4) << 6) + (row & 15));
+      af[i][0] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (2 * lh));
+      af[i][1] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (2 * lh + 1));
+    }
+    float bf[TB][8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int k = 8 * lh + p;
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        const int col = wn0 + 32 * j + li;
+        const int q = (col >> 2) ^ (lh ? 8 : 0);
+        bf[j][p] = bs[4 * (k * QB + q) + (col & 3)];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
+    st = (st == 2) ? 0 : st + 1;
+  }
+
+#pragma unroll
+  for (int i = 0; i < TA; ++i) {
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int col = n0 + wn0 + 32 * j + li;
+      const bool col_ok = col < g.N;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const bool ok = col_ok && row < g.M;
+        store1(rc, ok ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob,
+               acc[i][j][r]);
+      }
+    }
+  }
+}
+
+}  // namespace sg

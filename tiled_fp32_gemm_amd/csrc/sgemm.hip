@@ -8,6 +8,7 @@
 #include "../../include/sgemm.h"
 #include "kernel_fma.hpp"
 #include "kernel_mfma.hpp"
+#include "kernel_mfma_direct.hpp"
 #include "kernel_simple.hpp"
 
 namespace {
@@ -39,7 +40,7 @@ bool overlaps(const void* p, int64_t pb, const void* q, int64_t qb) {
 int check(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
           const float* B, int64_t ldb, const float* C, int64_t ldc, int algo,
           Checked& out) {
-  if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA) return SGEMM_ERR_INVALID_ARG;
+  if (algo < SGEMM_ALGO_AUTO || algo > SGEMM_ALGO_MFMA_DIRECT) return SGEMM_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_INVALID_ARG;
   if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_INVALID_ARG;
@@ -57,6 +58,10 @@ int check(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   for (auto& o : ops)
     if (o.bytes < 0 || o.bytes >= kMaxOperandBytes) return SGEMM_ERR_UNSUPPORTED;
   if (overlaps(C, cb, A, ab) || overlaps(C, cb, B, bb)) return SGEMM_ERR_INVALID_ARG;
+  if (algo == SGEMM_ALGO_MFMA_DIRECT && touch && K > 0 &&
+      !(((uintptr_t)A & 15u) == 0 && lda % 4 == 0 && K % 4 == 0 &&
+        ((uintptr_t)B & 15u) == 0 && ldb % 4 == 0 && N % 4 == 0))
+    return SGEMM_ERR_UNSUPPORTED;
   out.a_bytes = ab;
   out.b_bytes = bb;
   out.c_bytes = cb;
@@ -73,12 +78,83 @@ struct Plan {
   KernelFn fn;
 };
 
+bool vec_a_ok(const float* A, int64_t lda, int64_t K) {
+  return aligned16(A) && lda % 4 == 0 && K % 4 == 0;
+}
+bool vec_b_ok(const float* B, int64_t ldb, int64_t N) {
+  return aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+}
+
+// One launchable configuration of a kernel family.
+struct Variant {
+  const char* name;
+  int tile_m, tile_n, tile_k, threads, lds_bytes;
+  KernelFn vv, sv, vs, ss;  // by (A 128-bit?, B 128-bit?); null: unsupported
+};
+
+template <int BM, int BN, int WM, int WN, int BK>
+Variant reg_variant(const char* name) {
+  using Cfg = sg::MfmaCfg<BM, BN, WM, WN, BK>;
+  return {name, BM, BN, BK, Cfg::NT, Cfg::LDS_FLOATS * 4,
+          sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, true, true>,
+          sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, true>,
+          sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, true, false>,
+          sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, false>};
+}
+
 template <int BM, int BN, int WM, int WN>
-KernelFn mfma_fn(bool va, bool vb) {
-  if (va && vb) return sg::sgemm_mfma_kernel<BM, BN, WM, WN, true, true>;
-  if (va) return sg::sgemm_mfma_kernel<BM, BN, WM, WN, true, false>;
-  if (vb) return sg::sgemm_mfma_kernel<BM, BN, WM, WN, false, true>;
-  return sg::sgemm_mfma_kernel<BM, BN, WM, WN, false, false>;
+Variant direct_variant(const char* name) {
+  using Cfg = sg::DirectCfg<BM, BN, WM, WN>;
+  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4,
+          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN>, nullptr, nullptr, nullptr};
+}
+
+// Matrix-core configurations, large to small tiles, each with its measured
+// steady-state rate on MI355X in TFLOP/s (8192^3, one kernel per launch).
+// The large tiles cut L2 traffic per flop; the small ones keep more CUs busy
+// on small or ragged shapes.
+struct Candidate {
+  Variant v;
+  double tflops;
+};
+
+const Candidate* mfma_candidates(bool direct, int& n) {
+  static const Candidate reg[3] = {
+      {reg_variant<256, 128, 64, 64, 16>("mfma_256x128x16"), 139.0},
+      {reg_variant<128, 128, 64, 32, 16>("mfma_128x128x16"), 135.0},
+      {reg_variant<64, 64, 32, 32, 16>("mfma_64x64x16"), 119.0}};
+  static const Candidate lds[3] = {
+      {direct_variant<256, 256, 64, 64>("mfma_lds_256x256x16"), 141.0},
+      {direct_variant<128, 128, 64, 32>("mfma_lds_128x128x16"), 140.0},
+      {direct_variant<64, 64, 32, 32>("mfma_lds_64x64x16"), 125.0}};
+  n = 3;
+  return direct ? lds : reg;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kCUs = 256;  // MI355X compute units
+
+// The candidate with the least estimated time.  Workgroups are spread evenly
+// over the CUs, so the busiest CU computes ceil(tiles / CUs) tiles, each
+// BM x BN x K at the variant's rate: time ~ ceil(tiles / CUs) * BM * BN /
+// rate.  This charges the padding of partial tiles and the idle CUs of the
+// last round of tiles (wave quantisation).  Ties keep the larger tile.
+const Variant& choose_mfma(int64_t M, int64_t N, bool direct) {
+  int n;
+  const Candidate* c = mfma_candidates(direct, n);
+  int best = 0;
+  double best_t = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t tiles = cdiv(M, c[i].v.tile_m) * cdiv(N, c[i].v.tile_n);
+    const double t = (double)cdiv(tiles, kCUs) * c[i].v.tile_m * c[i].v.tile_n /
+                     c[i].tflops;
+    if (i == 0 || t < best_t * 0.995) {
+      best = i;
+      best_t = t;
+    }
+  }
+  return c[best].v;
 }
 
 KernelFn fma_fn(bool va, bool vb, bool vc) {
@@ -91,59 +167,50 @@ KernelFn fma_fn(bool va, bool vb, bool vc) {
   return table[idx];
 }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-void set_name(sgemm_plan& p, const char* fam, bool va, bool vb) {
-  snprintf(p.kernel, sizeof(p.kernel), "%s_%dx%dx%d_%s%s", fam, p.tile_m,
-           p.tile_n, p.tile_k, va ? "va" : "sa", vb ? "vb" : "sb");
+void set_name(sgemm_plan& p, const char* base, bool va, bool vb) {
+  snprintf(p.kernel, sizeof(p.kernel), "%s_%s%s", base, va ? "va" : "sa",
+           vb ? "vb" : "sb");
 }
 
 // Chooses the kernel and fills the launch geometry for checked arguments.
+// algo must be valid; SGEMM_ALGO_MFMA_DIRECT must have 128-bit A and B.
 Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
               const float* B, int64_t ldb, const float* C, int64_t ldc,
               int algo) {
   Plan p;
   memset(&p, 0, sizeof(p));
-  const bool va = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
-  const bool vb = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+  // With K == 0 neither A nor B is read, so any load form will do.
+  const bool va = K == 0 || vec_a_ok(A, lda, K);
+  const bool vb = K == 0 || vec_b_ok(B, ldb, N);
   const bool vc = aligned16(C) && ldc % 4 == 0 && N % 4 == 0;
-  if (algo == SGEMM_ALGO_AUTO) algo = SGEMM_ALGO_MFMA;
+  if (algo == SGEMM_ALGO_AUTO)
+    algo = (va && vb) ? SGEMM_ALGO_MFMA_DIRECT : SGEMM_ALGO_MFMA;
   p.info.algo = algo;
-  p.info.tile_k = 16;
+  p.info.vec_a = va;
+  p.info.vec_b = vb;
   if (algo == SGEMM_ALGO_SIMPLE) {
-    p.info.tile_m = p.info.tile_n = sg::kSimpleT;
+    p.info.tile_m = p.info.tile_n = p.info.tile_k = sg::kSimpleT;
     p.info.threads = sg::kSimpleT * sg::kSimpleT;
     p.info.lds_bytes = 2 * sg::kSimpleT * sg::kSimpleT * 4;
+    p.info.vec_a = p.info.vec_b = 0;
     p.fn = sg::sgemm_simple_kernel;
     snprintf(p.info.kernel, sizeof(p.info.kernel), "simple_16x16x16");
   } else if (algo == SGEMM_ALGO_FMA) {
     p.info.tile_m = p.info.tile_n = 128;
+    p.info.tile_k = 16;
     p.info.threads = sg::FmaCfg::NT;
     p.info.lds_bytes = sg::FmaCfg::LDS_FLOATS * 4;
-    p.info.vec_a = va;
-    p.info.vec_b = vb;
     p.fn = fma_fn(va, vb, vc);
-    set_name(p.info, "fma", va, vb);
+    set_name(p.info, "fma_128x128x16", va, vb);
   } else {
-    // 128 x 128 tiles when they give every CU at least one; 64 x 64 tiles
-    // otherwise (small and ragged shapes), so that fewer CUs sit idle.
-    const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
-    if (t128 >= 256) {
-      using Cfg = sg::MfmaCfg<128, 128, 64, 64>;
-      p.info.tile_m = p.info.tile_n = 128;
-      p.info.threads = Cfg::NT;
-      p.info.lds_bytes = Cfg::LDS_FLOATS * 4;
-      p.fn = mfma_fn<128, 128, 64, 64>(va, vb);
-    } else {
-      using Cfg = sg::MfmaCfg<64, 64, 32, 32>;
-      p.info.tile_m = p.info.tile_n = 64;
-      p.info.threads = Cfg::NT;
-      p.info.lds_bytes = Cfg::LDS_FLOATS * 4;
-      p.fn = mfma_fn<64, 64, 32, 32>(va, vb);
-    }
-    p.info.vec_a = va;
-    p.info.vec_b = vb;
-    set_name(p.info, "mfma", va, vb);
+    const Variant& v = choose_mfma(M, N, algo == SGEMM_ALGO_MFMA_DIRECT);
+    p.info.tile_m = v.tile_m;
+    p.info.tile_n = v.tile_n;
+    p.info.tile_k = v.tile_k;
+    p.info.threads = v.threads;
+    p.info.lds_bytes = v.lds_bytes;
+    p.fn = va ? (vb ? v.vv : v.vs) : (vb ? v.sv : v.ss);
+    set_name(p.info, v.name, va, vb);
   }
   p.info.workgroups = (M > 0 && N > 0)
                           ? cdiv(M, p.info.tile_m) * cdiv(N, p.info.tile_n)
@@ -162,6 +229,7 @@ int sgemm_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   const int st = check(M, N, K, A, lda, B, ldb, C, ldc, algo, c);
   if (st != SGEMM_OK || !c.launch) return st;
   const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, algo);
+  if (p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;  // no kernel for this form
 
   GemmArgs g;
   g.A = A;
@@ -210,7 +278,9 @@ const char* sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "success";
     case SGEMM_ERR_INVALID_ARG: return "invalid argument";
-    case SGEMM_ERR_UNSUPPORTED: return "unsupported: an operand spans 2 GiB or more";
+    case SGEMM_ERR_UNSUPPORTED:
+      return "unsupported: an operand spans 2 GiB or more, or the LDS-direct "
+             "family was asked for rows that are not 128-bit aligned";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
