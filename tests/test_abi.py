@@ -116,17 +116,17 @@ def test_k_zero_plans_a_zero_fill(lib, algo):
 
 
 @pytest.mark.parametrize("M,N,K,lda,ldb,aoff,kernel,wgs", [
-    (4096, 4096, 4096, 4096, 4096, 0, "mfma_lds_256x256x16_vavb", 256),
-    (8192, 8192, 8192, 8192, 8192, 0, "mfma_lds_256x256x16_vavb", 1024),
-    (65536, 128, 256, 256, 128, 0, "mfma_lds_128x128x16_vavb", 512),
+    (4096, 4096, 4096, 4096, 4096, 0, "mfma_lds_256x256x32_vavb", 256),
+    (8192, 8192, 8192, 8192, 8192, 0, "mfma_lds_256x256x32_vavb", 1024),
+    (65536, 128, 256, 256, 128, 0, "mfma_lds_128x128x32_vavb", 512),
     (1000, 1500, 777, 777, 1500, 0, "mfma_64x64x16_savb", 384),
-    (256, 256, 256, 256, 256, 0, "mfma_lds_64x64x16_vavb", 16),
+    (256, 256, 256, 256, 256, 0, "mfma_lds_64x64x32_vavb", 16),
     (256, 256, 256, 256, 256, 4, "mfma_64x64x16_savb", 16),    # A 4B-aligned only
     (256, 256, 256, 258, 256, 0, "mfma_64x64x16_savb", 16),    # lda % 4 != 0
     (4096, 4096, 4095, 4095, 4096, 0, "mfma_256x128x16_savb", 512),
-    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x16_vavb", 2209),
-    (2048, 2048, 2048, 2048, 2048, 0, "mfma_lds_128x128x16_vavb", 256),
-    (4100, 4100, 4096, 4096, 4100, 0, "mfma_lds_64x64x16_vavb", 4225),
+    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x32_vavb", 2209),
+    (2048, 2048, 2048, 2048, 2048, 0, "mfma_lds_128x128x32_vavb", 256),
+    (4100, 4100, 4096, 4096, 4100, 0, "mfma_lds_64x64x32_vavb", 4225),
 ])
 def test_plans(lib, M, N, K, lda, ldb, aoff, kernel, wgs):
     st, plan = call(M, N, K, A=BIG + aoff, lda=lda, ldb=ldb,

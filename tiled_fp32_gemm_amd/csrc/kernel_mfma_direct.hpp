@@ -12,24 +12,25 @@
 // chosen as a permutation of 16-byte units that keeps every load instruction
 // lane-linear and every read conflict-free on 64 banks of 4 bytes:
 //
-//   A stage (BM x 16): rows in blocks of 16; inside a block the four k
-//     groups follow each other, row fastest: unit(r, c) = 64 (r / 16) +
+//   A stage (BM x BK): rows in blocks of 16; inside a block the BK/4 k
+//     groups follow each other, row fastest: unit(r, c) = 4 BK (r / 16) +
 //     16 c + r % 16.  A load instruction covers 16 rows x 64 contiguous
 //     bytes of global memory; an MFMA fragment read by 16 consecutive lanes
 //     (16 consecutive rows, one k group) is 256 contiguous bytes.
-//   B stage (16 x BN): rows as in memory with the 16-byte units of rows 8..15
-//     XOR-swizzled by 8: unit(k, q) = k BN/4 + (q ^ 8 [k >= 8]).  The 32-bit
-//     reads give lanes 0-31 row p and lanes 32-63 row 8 + p; the swizzle puts
+//   B stage (BK x BN): rows as in memory with the 16-byte units of rows whose
+//     bit 3 is set XOR-swizzled by 8: unit(k, q) = k BN/4 + (q ^ 8 [k & 8]).
+//     The 32-bit reads give lanes 0-31 row 16 s + p and lanes 32-63 row
+//     16 s + 8 + p of sub-slab s; the swizzle puts
 //     the two halves on the two disjoint halves of the banks (the pages' XOR
 //     swizzle idea, "Memory-bank mechanism and accelerated compute", section
 //     on alternatives to padding, applied at 16-byte granularity so that the
 //     128-bit units stay whole).
 //
 // Out-of-range lanes read 0 into LDS (buffer range check), which gives the
-// zero-filled edges.  Pipeline: slabs t and t+1 are in flight while slab t is
-// computed; at the top of each step a wave waits until its own loads of slab
-// t have landed, then one barrier makes every wave's loads visible and frees
-// the stage of slab t-1 for slab t+2.  Requires 128-bit-capable A and B rows
+// zero-filled edges.  Pipeline with S stages: up to S - 1 slabs are in flight
+// while slab t is computed; at the top of each step a wave waits until its
+// own loads of slab t have landed, then one barrier makes every wave's loads
+// visible and frees the stage of slab t-1 for slab t + S - 1.  Requires 128-bit-capable A and B rows
 // (16-byte aligned, leading dimension and row length multiples of 4).
 #pragma once
 
@@ -37,9 +38,12 @@
 
 namespace sg {
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3>
 struct DirectCfg {
-  static constexpr int BK = 16, STAGES = 3;
+  static constexpr int BK = BK_, STAGES = STAGES_;
+  static constexpr int DEPTH = STAGES - 1;  // slabs loaded ahead
+  static constexpr int SUB = BK / 16;       // 16-deep sub-slabs per slab
+  static constexpr int CPR = BK / 4;        // 16-byte k groups per A row
   static constexpr int WAVES_N = BN / WN;
   static constexpr int NT = 64 * (BM / WM) * (BN / WN);
   static constexpr int TA = WM / 32, TB = WN / 32;
@@ -52,21 +56,39 @@ struct DirectCfg {
   static_assert(A_SLOTS * NT * 4 == BM * BK && B_SLOTS * NT * 4 == BK * BN,
                 "slabs must split into whole 64-lane load instructions");
   static_assert(BM % 32 == 0 && BN >= 64 && BN % 64 == 0, "tile shape");
-  static_assert(LOADS < 16, "wait count must fit the low field");
+  static_assert(LOADS * DEPTH < 64, "wait count must fit the 6-bit field");
+  static_assert(BK % 16 == 0 && STAGES >= 2, "slab depth and stages");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima; the
+// 6-bit vector-memory count is split over bits 3:0 and 15:14).
 template <int n>
 struct VmWait {
-  static constexpr int imm = (n & 0xF) | (0x7 << 4) | (0xF << 8);
+  static_assert(n >= 0 && n < 64, "vector-memory count is 6 bits");
+  static constexpr int imm = (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
 };
 
-template <int BM, int BN, int WM, int WN>
+// Waits until at most `ahead` slabs of this wave's loads are still in flight.
+template <int LOADS, int DEPTH>
+__device__ __forceinline__ void wait_slabs(int ahead) {
+  if constexpr (DEPTH >= 3) {
+    if (ahead >= 2) { __builtin_amdgcn_s_waitcnt(VmWait<2 * LOADS>::imm); return; }
+  }
+  if constexpr (DEPTH >= 2) {
+    if (ahead >= 1) { __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::imm); return; }
+  }
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+}
+
+template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3, bool PRIO = false>
 __global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN))
 sgemm_mfma_direct_kernel(GemmArgs g) {
-  using Cfg = DirectCfg<BM, BN, WM, WN>;
+  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, STAGES_>;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
+  constexpr int SUB = Cfg::SUB, CPR = Cfg::CPR, STAGES = Cfg::STAGES;
+  constexpr int DEPTH = Cfg::DEPTH;
+  static_assert(DEPTH <= 3, "at most three slabs ahead");
   constexpr int QB = BN / 4;  // 16-byte units per B row
 
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
@@ -95,7 +117,7 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
 #pragma unroll
   for (int s = 0; s < Cfg::A_SLOTS; ++s) {
     const int u = s * NT + 64 * wave + lane;
-    const int row = ((u >> 6) << 4) + (u & 15), c = (u >> 4) & 3;
+    const int row = (u / (16 * CPR)) * 16 + (u & 15), c = (u >> 4) % CPR;
     a_row_ok[s] = (m0 + row) < g.M;
     a_k[s] = 4 * c;
     a_off[s] = ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u;
@@ -137,52 +159,57 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nslab = (g.K + BK - 1) / BK;
-  if (nslab > 0) issue(0, 0);
-  if (nslab > 1) issue(BK, 1);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nslab) issue(d * BK, d);
 
   int st = 0;  // stage of slab t
   for (int t = 0; t < nslab; ++t) {
-    if (t + 1 < nslab)
-      __builtin_amdgcn_s_waitcnt(VmWait<Cfg::LOADS>::imm);
-    else
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    const int ahead = min(DEPTH - 1, nslab - 1 - t);  // later slabs in flight
+    wait_slabs<Cfg::LOADS, DEPTH>(ahead);
     // A plain workgroup barrier: the wait above already covers this wave's
     // loads of slab t, and the "memory" clobber keeps the compiler from
     // moving LDS accesses across it.  (A full __syncthreads() fence would
-    // also wait for slab t+1, which must stay in flight.)
+    // also wait for the later slabs, which must stay in flight.)
     asm volatile("s_barrier" ::: "memory");
-    if (t + 2 < nslab) issue((t + 2) * BK, st == 0 ? 2 : st - 1);
+    if (t + DEPTH < nslab)
+      issue((t + DEPTH) * BK, st == 0 ? STAGES - 1 : st - 1);
 
     const float* as = As + st * Cfg::A_STAGE;
     const float* bs = Bs + st * Cfg::B_STAGE;
-    f32x4 af[TA][2];
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < TA; ++i) {
-      const int row = wm0 + 32 * i + li;
-      const float* p = as + 4 * (((row >> 4) << 6) + (row & 15));
-      af[i][0] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (2 * lh));
-      af[i][1] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (2 * lh + 1));
-    }
-    float bf[TB][8];
+    for (int sub = 0; sub < SUB; ++sub) {
+      f32x4 af[TA][2];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int k = 8 * lh + p;
-#pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        const int col = wn0 + 32 * j + li;
-        const int q = (col >> 2) ^ (lh ? 8 : 0);
-        bf[j][p] = bs[4 * (k * QB + q) + (col & 3)];
+      for (int i = 0; i < TA; ++i) {
+        const int row = wm0 + 32 * i + li;
+        const float* p = as + 4 * ((row >> 4) * (16 * CPR) + (row & 15));
+        af[i][0] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh));
+        af[i][1] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + 1));
       }
+      float bf[TB][8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int k = 16 * sub + 8 * lh + p;
+#pragma unroll
+        for (int j = 0; j < TB; ++j) {
+          const int col = wn0 + 32 * j + li;
+          const int q = (col >> 2) ^ (lh ? 8 : 0);
+          bf[j][p] = bs[4 * (k * QB + q) + (col & 3)];
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+#pragma unroll
+        for (int i = 0; i < TA; ++i)
+#pragma unroll
+          for (int j = 0; j < TB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-#pragma unroll
-      for (int i = 0; i < TA; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-              af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
-    st = (st == 2) ? 0 : st + 1;
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    st = (st == STAGES - 1) ? 0 : st + 1;
   }
 
 #pragma unroll

@@ -102,11 +102,12 @@ Variant reg_variant(const char* name) {
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, false>};
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 Variant direct_variant(const char* name) {
-  using Cfg = sg::DirectCfg<BM, BN, WM, WN>;
+  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, STAGES>;
   return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4,
-          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN>, nullptr, nullptr, nullptr};
+          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES>, nullptr,
+          nullptr, nullptr};
 }
 
 // Matrix-core configurations, large to small tiles, each with its measured
@@ -123,10 +124,12 @@ const Candidate* mfma_candidates(bool direct, int& n) {
       {reg_variant<256, 128, 64, 64, 16>("mfma_256x128x16"), 139.0},
       {reg_variant<128, 128, 64, 32, 16>("mfma_128x128x16"), 135.0},
       {reg_variant<64, 64, 32, 32, 16>("mfma_64x64x16"), 119.0}};
+  // LDS-direct: 32-deep slabs in two stages (one slab in flight) halve the
+  // barriers per flop against 16-deep slabs in three stages.
   static const Candidate lds[3] = {
-      {direct_variant<256, 256, 64, 64>("mfma_lds_256x256x16"), 141.0},
-      {direct_variant<128, 128, 64, 32>("mfma_lds_128x128x16"), 140.0},
-      {direct_variant<64, 64, 32, 32>("mfma_lds_64x64x16"), 125.0}};
+      {direct_variant<256, 256, 64, 64, 32, 2>("mfma_lds_256x256x32"), 144.9},
+      {direct_variant<128, 128, 64, 32, 32, 2>("mfma_lds_128x128x32"), 137.3},
+      {direct_variant<64, 64, 32, 32, 32, 2>("mfma_lds_64x64x32"), 126.3}};
   n = 3;
   return direct ? lds : reg;
 }
