@@ -46,9 +46,7 @@
  *                          non-empty operand; C overlapping A or B; an
  *                          unknown algo.
  *   SGEMM_ERR_UNSUPPORTED  an operand spans 2 GiB or more (the kernels
- *                          address each operand with 32-bit byte offsets),
- *                          or SGEMM_ALGO_MFMA_DIRECT was asked for rows
- *                          that do not allow 128-bit loads.
+ *                          address each operand with 32-bit byte offsets).
  *   SGEMM_ERR_LAUNCH       the HIP launch reported an error.
  * M == 0 or N == 0 returns SGEMM_OK with nothing enqueued; K == 0 writes
  * C = 0 (the empty sum).
@@ -80,9 +78,8 @@ extern "C" {
 #define SGEMM_ERR_LAUNCH 3
 
 /* Kernel families (sgemm_ex).
- *   AUTO    the fastest family for the arguments: MFMA_DIRECT when A and B
- *           rows allow 128-bit loads, else MFMA; the tile size follows the
- *           shape.
+ *   AUTO    the fastest family, MFMA_DIRECT, with the tile size (and the
+ *           split of K across wave groups) chosen from the shape.
  *   SIMPLE  one output per thread from 16x16 shared tiles, the basic tiled
  *           inner loop of "CUDA in depth (4): accessing shared memory
  *           efficiently", section on too many shared-memory reads.
@@ -93,10 +90,11 @@ extern "C" {
  *           instruction (32x32x2, fused multiply-add in FP32, round to
  *           nearest even); any alignment.
  *   MFMA_DIRECT  the same matrix instructions with slabs loaded from global
- *           memory straight into LDS (three LDS stages); needs A and B
- *           16-byte aligned with lda, K, ldb and N multiples of 4
- *           ("CUDA in depth (5)", section on contiguity and alignment),
- *           else SGEMM_ERR_UNSUPPORTED.  Bitwise equal to MFMA. */
+ *           memory straight into LDS in 16-byte groups (any 4-byte
+ *           alignment; the groups that straddle k = K are zero-filled in
+ *           LDS).  Bitwise equal to MFMA when K is not split across wave
+ *           groups; otherwise the partial sums of the groups are added in a
+ *           fixed order. */
 #define SGEMM_ALGO_AUTO 0
 #define SGEMM_ALGO_SIMPLE 1
 #define SGEMM_ALGO_FMA 2

@@ -52,17 +52,11 @@ def vec_rows(ptr: int, ld: int, width: int) -> bool:
 
 def run(M, N, K, dA: DevMat, dB: DevMat, dC: DevMat, algo="auto",
         stream=None, sync=True) -> bool:
-    """One call through the C ABI.  Returns False (after checking the
-    documented refusal) when the LDS-direct family is asked for rows that
-    are not 128-bit capable; True once the product has run."""
+    """One call through the C ABI; True once the product has run."""
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     st = sg.sgemm_ex(M, N, K, dA.ptr, dA.ld, dB.ptr, dB.ld, dC.ptr, dC.ld,
                      s.cuda_stream, sg.ALGOS[algo])
-    if (algo == "mfma_direct" and M > 0 and N > 0 and K > 0
-            and not (vec_rows(dA.ptr, dA.ld, K) and vec_rows(dB.ptr, dB.ld, N))):
-        assert st == sg.ERR_UNSUPPORTED, sg.sgemm_status_string(st)
-        return False
     assert st == sg.OK, sg.sgemm_status_string(st)
     if sync:
         torch.cuda.synchronize()

@@ -76,9 +76,6 @@ def call(M, N, K, A=BIG, lda=None, B=BIG + (1 << 31), ldb=None,
     (dict(M=4, N=4, K=4, C=BIG + 16), sg.ERR_INVALID_ARG),  # C overlaps A
     (dict(M=4, N=4, K=4, B=BIG + (1 << 32) + 60), sg.ERR_INVALID_ARG),  # B overlaps C
     (dict(M=4, N=4, K=4, algo=5), sg.ERR_INVALID_ARG),
-    (dict(M=4, N=4, K=4, A=BIG + 4, algo=4), sg.ERR_UNSUPPORTED),  # direct, A not 16B
-    (dict(M=4, N=4, K=6, lda=6, algo=4), sg.ERR_UNSUPPORTED),      # direct, K % 4
-    (dict(M=4, N=6, K=4, ldb=6, ldc=6, algo=4), sg.ERR_UNSUPPORTED),  # direct, N % 4
     (dict(M=4, N=4, K=4, algo=-1), sg.ERR_INVALID_ARG),
     (dict(M=1 << 15, N=4, K=1 << 14), sg.ERR_UNSUPPORTED),  # A spans 2 GiB
     (dict(M=(1 << 31) // 4096 + 1, N=1024, K=4, ldc=1024), sg.ERR_UNSUPPORTED),
@@ -119,22 +116,29 @@ def test_k_zero_plans_a_zero_fill(lib, algo):
     (4096, 4096, 4096, 4096, 4096, 0, "mfma_lds_256x256x32_vavb", 256),
     (8192, 8192, 8192, 8192, 8192, 0, "mfma_lds_256x256x32_vavb", 1024),
     (65536, 128, 256, 256, 128, 0, "mfma_lds_128x128x32_vavb", 512),
-    (1000, 1500, 777, 777, 1500, 0, "mfma_64x64x16_savb", 384),
-    (256, 256, 256, 256, 256, 0, "mfma_lds_64x64x32_vavb", 16),
-    (256, 256, 256, 256, 256, 4, "mfma_64x64x16_savb", 16),    # A 4B-aligned only
-    (256, 256, 256, 258, 256, 0, "mfma_64x64x16_savb", 16),    # lda % 4 != 0
-    (4096, 4096, 4095, 4095, 4096, 0, "mfma_256x128x16_savb", 512),
-    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x32_vavb", 2209),
+    (1000, 1500, 777, 777, 1500, 0, "mfma_lds_32x64x32_ks2_savb", 768),
+    (256, 256, 256, 256, 256, 0, "mfma_lds_32x64x64_ks4_vavb", 32),
+    (256, 256, 256, 256, 256, 4, "mfma_lds_32x64x64_ks4_savb", 32),  # A 4B-aligned
+    (256, 256, 256, 258, 256, 0, "mfma_lds_32x64x64_ks4_savb", 32),  # lda % 4 != 0
+    (4096, 4096, 4095, 4095, 4096, 0, "mfma_lds_256x256x32_savb", 256),
+    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x32_ks2_vavb", 2209),
     (2048, 2048, 2048, 2048, 2048, 0, "mfma_lds_128x128x32_vavb", 256),
-    (4100, 4100, 4096, 4096, 4100, 0, "mfma_lds_64x64x32_vavb", 4225),
+    (512, 4096, 4096, 4096, 4096, 0, "mfma_lds_64x128x32_ks2_vavb", 256),
+    (384, 4096, 64, 64, 4096, 0, "mfma_lds_32x64x32_ks2_vavb", 768),
 ])
 def test_plans(lib, M, N, K, lda, ldb, aoff, kernel, wgs):
     st, plan = call(M, N, K, A=BIG + aoff, lda=lda, ldb=ldb,
                     B=BIG + (1 << 31), C=BIG + (1 << 32))
     assert st == sg.OK
     assert plan.kernel.decode() == kernel and plan.workgroups == wgs
-    direct = kernel.startswith("mfma_lds")
-    assert plan.algo == sg.ALGOS["mfma_direct" if direct else "mfma"]
+    assert plan.algo == sg.ALGOS["mfma_direct"]
+
+
+def test_register_staged_family_plans(lib):
+    st, plan = call(1000, 1500, 777, lda=777, algo=sg.ALGOS["mfma"])
+    assert st == sg.OK and plan.kernel.decode() == "mfma_64x64x16_savb"
+    st, plan = call(4096, 4096, 4096, algo=sg.ALGOS["mfma"])
+    assert st == sg.OK and plan.kernel.decode() == "mfma_256x128x16_vavb"
 
 
 def test_plans_per_family(lib):

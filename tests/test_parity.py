@@ -233,6 +233,35 @@ def test_largest_operand(K):
     del dA, dC
 
 
+# One shape per LDS-direct variant the planner can pick (the test checks the
+# pick), each with K not a multiple of 4 so that the straddling A groups are
+# zero-filled, and with an odd lda so that A rows are only 4-byte aligned.
+VARIANT_SHAPES = [
+    ("mfma_lds_256x256x32", 4096, 4096, 22),
+    ("mfma_lds_128x128x32", 1024, 4096, 38),
+    ("mfma_lds_64x128x32_ks2", 512, 4096, 45),
+    ("mfma_lds_64x64x32_ks2", 3072, 192, 53),
+    ("mfma_lds_32x64x32_ks2", 384, 4096, 61),
+    ("mfma_lds_32x64x64_ks4", 32, 64, 67),
+]
+
+
+@pytest.mark.parametrize("kernel,M,N,K", VARIANT_SHAPES, ids=[v[0] for v in VARIANT_SHAPES])
+@pytest.mark.parametrize("odd_lda", [False, True])
+def test_every_direct_variant(kernel, M, N, K, odd_lda):
+    import tiled_fp32_gemm_amd as sg
+    lda = K + (3 if odd_lda else 1)
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 1700 + K, lda=lda, fill=np.nan)
+    dA, dB = DevMat(A), DevMat(B)
+    dC = DevMat(np.full((M, N), np.nan, np.float32))
+    st, plan = sg.sgemm_plan_query(M, N, K, dA.ptr, lda, dB.ptr, N, dC.ptr, N, 0)
+    assert st == sg.OK and plan.kernel.decode().rsplit("_", 1)[0] == kernel
+    say(f"[gpu] variant {kernel} M={M} N={N} K={K} lda={lda}")
+    assert run(M, N, K, dA, dB, dC, "auto")
+    Cref, T = oracle.gemm(A[:, :K], B, M=M, N=N, K=K)
+    assert_close(dC.host(), Cref, T, kernel)
+
+
 def test_matmul_wrapper_on_views():
     """The tensor convenience: row-stride views and the current stream."""
     import tiled_fp32_gemm_amd as sg

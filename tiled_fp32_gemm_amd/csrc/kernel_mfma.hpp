@@ -28,6 +28,10 @@
 //                   lanes 0-31 one row and lanes 32-63 the row 8 below, and
 //                   8 * (BN + 4) = 32 (mod 64) puts the two halves on
 //                   disjoint banks.
+//  * Split K inside the workgroup (KS > 1, for shapes with too few tiles to
+//    fill the chip): KS wave groups each compute the same BM x BN tile over
+//    their own share of every slab's sub-slabs, and the partial tiles are
+//    summed through LDS at the end.
 //  * The k order inside each 16-deep sub-slab is regrouped: MFMA step p (0..7)
 //    takes k = p from lanes 0-31 and k = 8 + p from lanes 32-63.  Every k is
 //    still used exactly once for A and B alike, and each lane's eight A values
@@ -44,21 +48,27 @@
 
 namespace sg {
 
-template <int BM, int BN, int WM, int WN, int BK_ = 16>
+template <int BM, int BN, int WM, int WN, int BK_ = 16, int KS_ = 1>
 struct MfmaCfg {
   static constexpr int BK = BK_;
+  static constexpr int KS = KS_;       // wave groups sharing each slab
   static constexpr int SUB = BK / 16;  // 16-deep sub-slabs per slab
+  static constexpr int SUB_G = SUB / KS;  // ... per wave group
   static constexpr int CPR = BK / 4;   // 4-float groups per A tile row
   static constexpr int WAVES_M = BM / WM;
   static constexpr int WAVES_N = BN / WN;
-  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int SPATIAL = WAVES_M * WAVES_N;  // waves per group
+  static constexpr int NT = 64 * SPATIAL * KS;
   static constexpr int TA = WM / 32;  // 32x32 blocks per wave along M
   static constexpr int TB = WN / 32;  // ... along N
   static constexpr int RA = BK + 4;   // As row stride (floats)
   static constexpr int RB = BN + 4;   // Bs row stride (floats)
   static constexpr int A_STAGE = BM * RA;
   static constexpr int B_STAGE = BK * RB;
-  static constexpr int LDS_FLOATS = 2 * (A_STAGE + B_STAGE);
+  static constexpr int STAGE_FLOATS = 2 * (A_STAGE + B_STAGE);
+  static constexpr int RED_FLOATS = (KS - 1) * BM * BN;  // partial tiles
+  static constexpr int LDS_FLOATS =
+      STAGE_FLOATS > RED_FLOATS ? STAGE_FLOATS : RED_FLOATS;
   static constexpr int A_SLOTS = BM * BK / 4 / NT;  // 4-float groups per thread
   static constexpr int B_SLOTS = BK * BN / 4 / NT;
   static_assert(BM % WM == 0 && BN % WN == 0, "wave tiles must divide the tile");
@@ -69,6 +79,7 @@ struct MfmaCfg {
   static_assert((8 * RB) % 64 == 32, "B read halves must use disjoint banks");
   static_assert((RA / 4) % 2 == 1, "A row stride must be an odd number of 16B");
   static_assert(BK % 16 == 0 && BK <= 64, "slabs are whole 16-deep sub-slabs");
+  static_assert(SUB % KS == 0, "each wave group takes whole sub-slabs");
 };
 
 // One 4-float group of the A slab: slot s of thread t covers A tile row
@@ -81,12 +92,13 @@ __device__ __forceinline__ void a_slot(int f, int& row, int& kq) {
   kq = (f >> 4) % Cfg::CPR;
 }
 
-template <int BM, int BN, int WM, int WN, int BK_, bool VEC_A, bool VEC_B>
-__global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN))
+template <int BM, int BN, int WM, int WN, int BK_, bool VEC_A, bool VEC_B,
+          int KS_ = 1>
+__global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN) * KS_)
 sgemm_mfma_kernel(GemmArgs g) {
-  using Cfg = MfmaCfg<BM, BN, WM, WN, BK_>;
+  using Cfg = MfmaCfg<BM, BN, WM, WN, BK_, KS_>;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
-  constexpr int SUB = Cfg::SUB;
+  constexpr int KS = Cfg::KS, SUB_G = Cfg::SUB_G;
   constexpr int RA = Cfg::RA, RB = Cfg::RB;
 
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
@@ -98,8 +110,9 @@ sgemm_mfma_kernel(GemmArgs g) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave / Cfg::WAVES_N) * WM;
-  const int wn0 = (wave % Cfg::WAVES_N) * WN;
+  const int grp = wave / Cfg::SPATIAL, sw = wave % Cfg::SPATIAL;
+  const int wm0 = (sw / Cfg::WAVES_N) * WM;
+  const int wn0 = (sw % Cfg::WAVES_N) * WN;
   const int li = lane & 31, lh = lane >> 5;
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
@@ -196,7 +209,8 @@ sgemm_mfma_kernel(GemmArgs g) {
     const float* as = As + cur * Cfg::A_STAGE;
     const float* bs = Bs + cur * Cfg::B_STAGE;
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) {
+    for (int uu = 0; uu < SUB_G; ++uu) {
+      const int u = grp * SUB_G + uu;  // this wave group's sub-slabs
       f32x4 af[TA][2];
 #pragma unroll
       for (int i = 0; i < TA; ++i) {
@@ -223,6 +237,35 @@ sgemm_mfma_kernel(GemmArgs g) {
 
     if (more) store_slab(cur ^ 1);
     __syncthreads();
+  }
+
+  // Split K across wave groups: groups 1..KS-1 leave their partial tiles in
+  // LDS (lane-contiguous, so conflict-free), group 0 adds them in group order
+  // (a fixed order, so the result is run-to-run deterministic) and stores.
+  if constexpr (KS > 1) {
+    float* red = lds;  // the staging stages are free after the last barrier
+    constexpr int PER_WAVE = TA * TB * 16 * 64;
+    if (grp > 0) {
+      float* dst = red + ((grp - 1) * Cfg::SPATIAL + sw) * PER_WAVE + lane;
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * TB + j) * 16 + r) * 64] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;  // no barrier follows
+#pragma unroll
+    for (int q = 1; q < KS; ++q) {
+      const float* src = red + ((q - 1) * Cfg::SPATIAL + sw) * PER_WAVE + lane;
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * TB + j) * 16 + r) * 64];
+    }
   }
 
   // Epilogue: each lane writes column n0 + wn0 + 32 j + li of 16 rows per

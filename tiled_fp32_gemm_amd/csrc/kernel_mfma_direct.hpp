@@ -1,12 +1,26 @@
 // kernel_mfma_direct.hpp -- FP32 MFMA GEMM with direct global->LDS staging.
 //
-// Same tiles, MFMA microkernel, k regrouping and epilogue as
-// kernel_mfma.hpp, but the slabs go from global memory straight into LDS
-// with the gfx950 buffer-load-to-LDS form (128 bits per lane), bypassing
-// registers.  That is the nearest CDNA4 counterpart of the asynchronous copy
-// the pages mention ("Memory-bank mechanism and accelerated compute", section
-// on alternatives to padding); here it removes the staging registers and the
-// LDS store instructions, and lets three LDS stages keep two slabs in flight.
+// Same MFMA microkernel, k regrouping and epilogue as kernel_mfma.hpp, but
+// the slabs go from global memory straight into LDS with the gfx950
+// buffer-load-to-LDS form (16 bytes per lane), bypassing registers.  That is
+// the nearest CDNA4 counterpart of the asynchronous copy the pages mention
+// ("Memory-bank mechanism and accelerated compute", section on alternatives
+// to padding); here it removes the staging registers and the LDS store
+// instructions and keeps STAGES - 1 slabs in flight.
+//
+// Alignment.  The load-to-LDS form takes 16 bytes from any 4-byte-aligned
+// address and range-checks each 4-byte word against the resource, so rows of
+// any alignment and leading dimension are loaded as whole 4-float groups:
+//   * a B group reaching past column N-1 brings in values that only feed C
+//     columns >= N, which are never stored;
+//   * an A group reaching past row M-1 feeds only C rows >= M;
+//   * an A group that straddles k = K (possible in the last slab when K is
+//     not a multiple of 4) would bring in values from beyond the row, which
+//     meet the zero-filled B rows k >= K but could be NaN or Inf (a padding
+//     column, for instance): the lane that loaded such a group overwrites
+//     its words k >= K with 0 in LDS before the slab's barrier.  This is the
+//     pages' rule that an edge writes 0 for invalid elements ("CUDA in depth
+//     (5)", section on edges).
 //
 // A direct load writes lane l's 16 bytes at base + 16 l, so each layout is
 // chosen as a permutation of 16-byte units that keeps every load instruction
@@ -20,36 +34,44 @@
 //   B stage (BK x BN): rows as in memory with the 16-byte units of rows whose
 //     bit 3 is set XOR-swizzled by 8: unit(k, q) = k BN/4 + (q ^ 8 [k & 8]).
 //     The 32-bit reads give lanes 0-31 row 16 s + p and lanes 32-63 row
-//     16 s + 8 + p of sub-slab s; the swizzle puts
-//     the two halves on the two disjoint halves of the banks (the pages' XOR
-//     swizzle idea, "Memory-bank mechanism and accelerated compute", section
-//     on alternatives to padding, applied at 16-byte granularity so that the
+//     16 s + 8 + p of sub-slab s; the swizzle puts the two halves on the two
+//     disjoint halves of the banks (the pages' XOR swizzle idea,
+//     "Memory-bank mechanism and accelerated compute", section on
+//     alternatives to padding, applied at 16-byte granularity so that the
 //     128-bit units stay whole).
 //
-// Out-of-range lanes read 0 into LDS (buffer range check), which gives the
-// zero-filled edges.  Pipeline with S stages: up to S - 1 slabs are in flight
-// while slab t is computed; at the top of each step a wave waits until its
-// own loads of slab t have landed, then one barrier makes every wave's loads
-// visible and frees the stage of slab t-1 for slab t + S - 1.  Requires 128-bit-capable A and B rows
-// (16-byte aligned, leading dimension and row length multiples of 4).
+// Pipeline with S stages: up to S - 1 slabs are in flight while slab t is
+// computed; at the top of each step a wave waits until its own loads of slab
+// t have landed, then one barrier makes every wave's loads visible and frees
+// the stage of slab t-1 for slab t + S - 1.
+//
+// Split K inside the workgroup (KS > 1, for shapes with too few tiles to fill
+// the chip): KS wave groups compute the same tile over their own sub-slabs
+// of every slab; the partial tiles are summed through LDS in group order.
 #pragma once
 
 #include "common.hpp"
 
 namespace sg {
 
-template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3>
+template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3,
+          int KS_ = 1>
 struct DirectCfg {
-  static constexpr int BK = BK_, STAGES = STAGES_;
+  static constexpr int BK = BK_, STAGES = STAGES_, KS = KS_;
   static constexpr int DEPTH = STAGES - 1;  // slabs loaded ahead
   static constexpr int SUB = BK / 16;       // 16-deep sub-slabs per slab
+  static constexpr int SUB_G = SUB / KS;    // ... per wave group
   static constexpr int CPR = BK / 4;        // 16-byte k groups per A row
   static constexpr int WAVES_N = BN / WN;
-  static constexpr int NT = 64 * (BM / WM) * (BN / WN);
+  static constexpr int SPATIAL = (BM / WM) * (BN / WN);  // waves per group
+  static constexpr int NT = 64 * SPATIAL * KS;
   static constexpr int TA = WM / 32, TB = WN / 32;
   static constexpr int A_STAGE = BM * BK;   // floats
   static constexpr int B_STAGE = BK * BN;
-  static constexpr int LDS_FLOATS = STAGES * (A_STAGE + B_STAGE);
+  static constexpr int STAGE_FLOATS = STAGES * (A_STAGE + B_STAGE);
+  static constexpr int RED_FLOATS = (KS - 1) * BM * BN;
+  static constexpr int LDS_FLOATS =
+      STAGE_FLOATS > RED_FLOATS ? STAGE_FLOATS : RED_FLOATS;
   static constexpr int A_SLOTS = BM * BK / 4 / NT;
   static constexpr int B_SLOTS = BK * BN / 4 / NT;
   static constexpr int LOADS = A_SLOTS + B_SLOTS;  // vector loads per slab
@@ -57,7 +79,8 @@ struct DirectCfg {
                 "slabs must split into whole 64-lane load instructions");
   static_assert(BM % 32 == 0 && BN >= 64 && BN % 64 == 0, "tile shape");
   static_assert(LOADS * DEPTH < 64, "wait count must fit the 6-bit field");
-  static_assert(BK % 16 == 0 && STAGES >= 2, "slab depth and stages");
+  static_assert(BK % 16 == 0 && STAGES >= 2 && DEPTH <= 3, "slabs and stages");
+  static_assert(SUB % KS == 0, "each wave group takes whole sub-slabs");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -68,6 +91,10 @@ struct VmWait {
   static_assert(n >= 0 && n < 64, "vector-memory count is 6 bits");
   static constexpr int imm = (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
 };
+
+// s_waitcnt immediate that waits for every LDS access of this wave (lgkmcnt
+// 0, the other counts at their maxima).
+constexpr int kLdsWait = 0xF | (0x7 << 4) | (0x3 << 14);
 
 // Waits until at most `ahead` slabs of this wave's loads are still in flight.
 template <int LOADS, int DEPTH>
@@ -81,14 +108,14 @@ __device__ __forceinline__ void wait_slabs(int ahead) {
   __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
 }
 
-template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3, bool PRIO = false>
-__global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN))
+template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3,
+          int KS_ = 1>
+__global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN) * KS_)
 sgemm_mfma_direct_kernel(GemmArgs g) {
-  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, STAGES_>;
+  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, STAGES_, KS_>;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
-  constexpr int SUB = Cfg::SUB, CPR = Cfg::CPR, STAGES = Cfg::STAGES;
-  constexpr int DEPTH = Cfg::DEPTH;
-  static_assert(DEPTH <= 3, "at most three slabs ahead");
+  constexpr int CPR = Cfg::CPR, STAGES = Cfg::STAGES, DEPTH = Cfg::DEPTH;
+  constexpr int KS = Cfg::KS, SUB_G = Cfg::SUB_G;
   constexpr int QB = BN / 4;  // 16-byte units per B row
 
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
@@ -101,8 +128,9 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave / Cfg::WAVES_N) * WM;
-  const int wn0 = (wave % Cfg::WAVES_N) * WN;
+  const int grp = wave / Cfg::SPATIAL, sw = wave % Cfg::SPATIAL;
+  const int wm0 = (sw / Cfg::WAVES_N) * WM;
+  const int wn0 = (sw % Cfg::WAVES_N) * WN;
   const int li = lane & 31, lh = lane >> 5;
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
@@ -110,7 +138,7 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
 
   // Unit u = s NT + 64 wave + lane of each load instruction, and the global
-  // element it takes.
+  // 4-float group it takes.
   uint32_t a_off[Cfg::A_SLOTS];
   bool a_row_ok[Cfg::A_SLOTS];
   int a_k[Cfg::A_SLOTS];
@@ -134,7 +162,8 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
     b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u;
   }
 
-  // Issue the direct loads of the slab starting at k0 into stage st.
+  // Issue the direct loads of the slab starting at k0 into stage st.  A group
+  // is loaded when its first element is inside the matrix.
   auto issue = [&](int k0, int st) {
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
@@ -159,6 +188,7 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nslab = (g.K + BK - 1) / BK;
+  const bool k_ragged = (g.K & 3) != 0;  // an A group straddles k = K
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     if (d < nslab) issue(d * BK, d);
@@ -167,7 +197,19 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
   for (int t = 0; t < nslab; ++t) {
     const int ahead = min(DEPTH - 1, nslab - 1 - t);  // later slabs in flight
     wait_slabs<Cfg::LOADS, DEPTH>(ahead);
-    // A plain workgroup barrier: the wait above already covers this wave's
+    if (k_ragged && t == nslab - 1) {
+      // Zero this lane's own words k >= K of the straddling A group.
+#pragma unroll
+      for (int s = 0; s < Cfg::A_SLOTS; ++s) {
+        const int k = t * BK + a_k[s];
+        if (a_row_ok[s] && k < g.K && g.K < k + 4) {
+          float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + lane);
+          for (int e = g.K - k; e < 4; ++e) unit[e] = 0.0f;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kLdsWait);
+    }
+    // A plain workgroup barrier: the waits above already cover this wave's
     // loads of slab t, and the "memory" clobber keeps the compiler from
     // moving LDS accesses across it.  (A full __syncthreads() fence would
     // also wait for the later slabs, which must stay in flight.)
@@ -177,9 +219,9 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
 
     const float* as = As + st * Cfg::A_STAGE;
     const float* bs = Bs + st * Cfg::B_STAGE;
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int sub = 0; sub < SUB; ++sub) {
+    for (int uu = 0; uu < SUB_G; ++uu) {
+      const int sub = grp * SUB_G + uu;  // this wave group's sub-slabs
       f32x4 af[TA][2];
 #pragma unroll
       for (int i = 0; i < TA; ++i) {
@@ -208,8 +250,38 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                 af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
     }
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     st = (st == STAGES - 1) ? 0 : st + 1;
+  }
+
+  if constexpr (KS > 1) {
+    // Groups 1..KS-1 leave their partial tiles in LDS (lane-contiguous, so
+    // conflict-free) and group 0 adds them in group order (a fixed order, so
+    // the result is run-to-run deterministic).  The barrier first lets every
+    // wave finish reading the last stage.
+    __syncthreads();
+    float* red = lds;
+    constexpr int PER_WAVE = TA * TB * 16 * 64;
+    if (grp > 0) {
+      float* dst = red + ((grp - 1) * Cfg::SPATIAL + sw) * PER_WAVE + lane;
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * TB + j) * 16 + r) * 64] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (grp > 0) return;  // no barrier follows
+#pragma unroll
+    for (int q = 1; q < KS; ++q) {
+      const float* src = red + ((q - 1) * Cfg::SPATIAL + sw) * PER_WAVE + lane;
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * TB + j) * 16 + r) * 64];
+    }
   }
 
 #pragma unroll

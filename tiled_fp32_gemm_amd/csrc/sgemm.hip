@@ -58,10 +58,6 @@ int check(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   for (auto& o : ops)
     if (o.bytes < 0 || o.bytes >= kMaxOperandBytes) return SGEMM_ERR_UNSUPPORTED;
   if (overlaps(C, cb, A, ab) || overlaps(C, cb, B, bb)) return SGEMM_ERR_INVALID_ARG;
-  if (algo == SGEMM_ALGO_MFMA_DIRECT && touch && K > 0 &&
-      !(((uintptr_t)A & 15u) == 0 && lda % 4 == 0 && K % 4 == 0 &&
-        ((uintptr_t)B & 15u) == 0 && ldb % 4 == 0 && N % 4 == 0))
-    return SGEMM_ERR_UNSUPPORTED;
   out.a_bytes = ab;
   out.b_bytes = bb;
   out.c_bytes = cb;
@@ -102,18 +98,20 @@ Variant reg_variant(const char* name) {
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, false>};
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+// The LDS-direct kernel takes rows of any 4-byte alignment, so one kernel
+// serves every load form.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KS>
 Variant direct_variant(const char* name) {
-  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, STAGES>;
-  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4,
-          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES>, nullptr,
-          nullptr, nullptr};
+  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, STAGES, KS>;
+  const KernelFn f = sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES, KS>;
+  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, f, f, f, f};
 }
 
-// Matrix-core configurations, large to small tiles, each with its measured
-// steady-state rate on MI355X in TFLOP/s (8192^3, one kernel per launch).
-// The large tiles cut L2 traffic per flop; the small ones keep more CUs busy
-// on small or ragged shapes.
+// Matrix-core configurations, large to small tiles, each with its
+// steady-state rate on MI355X in TFLOP/s (measured at M = N = K = 4096 with
+// the chip full).  The large tiles cut L2 traffic per flop; the small ones,
+// and those that split K over wave groups, keep more of the chip busy on
+// small or ragged shapes.
 struct Candidate {
   Variant v;
   double tflops;
@@ -122,36 +120,58 @@ struct Candidate {
 const Candidate* mfma_candidates(bool direct, int& n) {
   static const Candidate reg[3] = {
       {reg_variant<256, 128, 64, 64, 16>("mfma_256x128x16"), 139.0},
-      {reg_variant<128, 128, 64, 32, 16>("mfma_128x128x16"), 135.0},
-      {reg_variant<64, 64, 32, 32, 16>("mfma_64x64x16"), 119.0}};
+      {reg_variant<128, 128, 64, 32, 16>("mfma_128x128x16"), 132.0},
+      {reg_variant<64, 64, 32, 32, 16>("mfma_64x64x16"), 125.0}};
   // LDS-direct: 32-deep slabs in two stages (one slab in flight) halve the
-  // barriers per flop against 16-deep slabs in three stages.
-  static const Candidate lds[3] = {
-      {direct_variant<256, 256, 64, 64, 32, 2>("mfma_lds_256x256x32"), 144.9},
-      {direct_variant<128, 128, 64, 32, 32, 2>("mfma_lds_128x128x32"), 137.3},
-      {direct_variant<64, 64, 32, 32, 32, 2>("mfma_lds_64x64x32"), 126.3}};
-  n = 3;
+  // barriers per flop against 16-deep slabs in three stages.  "ks" names the
+  // number of wave groups that split each slab.
+  static const Candidate lds[6] = {
+      {direct_variant<256, 256, 64, 64, 32, 2, 1>("mfma_lds_256x256x32"), 143.1},
+      {direct_variant<128, 128, 64, 32, 32, 2, 1>("mfma_lds_128x128x32"), 138.1},
+      {direct_variant<64, 128, 32, 64, 32, 2, 2>("mfma_lds_64x128x32_ks2"), 137.5},
+      {direct_variant<64, 64, 32, 32, 32, 2, 2>("mfma_lds_64x64x32_ks2"), 133.4},
+      {direct_variant<32, 64, 32, 32, 32, 2, 2>("mfma_lds_32x64x32_ks2"), 124.9},
+      {direct_variant<32, 64, 32, 32, 64, 2, 4>("mfma_lds_32x64x64_ks4"), 122.4}};
+  n = direct ? 6 : 3;
   return direct ? lds : reg;
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kCUs = 256;  // MI355X compute units
+constexpr int kCUs = 256;             // MI355X compute units
+constexpr int kLdsPerCU = 160 * 1024;  // bytes
+constexpr int kWavesPerCU = 16;        // at <= 128 VGPRs per lane
+constexpr double kSaturate = 2.0;      // waves per SIMD that keep MFMA busy
 
-// The candidate with the least estimated time.  Workgroups are spread evenly
-// over the CUs, so the busiest CU computes ceil(tiles / CUs) tiles, each
-// BM x BN x K at the variant's rate: time ~ ceil(tiles / CUs) * BM * BN /
-// rate.  This charges the padding of partial tiles and the idle CUs of the
-// last round of tiles (wave quantisation).  Ties keep the larger tile.
+// Estimated time (arbitrary units) of variant v on an M x N product.
+// Workgroups are spread evenly over the CUs, so the busiest CU computes
+// n = ceil(tiles / CUs) tiles of BM x BN (charging partial-tile padding and
+// the idle CUs of the last round, i.e. wave quantisation).  Up to `occ` of
+// them are resident at once (LDS and wave slots); with fewer than two waves
+// per SIMD resident, the matrix pipes idle in proportion.
+double estimate(const Candidate& c, int64_t M, int64_t N) {
+  const Variant& v = c.v;
+  const int64_t tiles = cdiv(M, v.tile_m) * cdiv(N, v.tile_n);
+  const int64_t n = cdiv(tiles, kCUs);
+  const int waves = v.threads / 64;
+  int occ = kLdsPerCU / v.lds_bytes;
+  if (occ > kWavesPerCU / waves) occ = kWavesPerCU / waves;
+  if (occ < 1) occ = 1;
+  const double resident = (double)(n < occ ? n : occ);
+  const double per_simd = resident * waves / 4.0;
+  const double busy = per_simd >= kSaturate ? 1.0 : per_simd / kSaturate;
+  return (double)n * v.tile_m * v.tile_n / (c.tflops * busy);
+}
+
+// The candidate with the least estimated time; ties keep the earlier
+// (larger-tile) one.
 const Variant& choose_mfma(int64_t M, int64_t N, bool direct) {
   int n;
   const Candidate* c = mfma_candidates(direct, n);
   int best = 0;
   double best_t = 0;
   for (int i = 0; i < n; ++i) {
-    const int64_t tiles = cdiv(M, c[i].v.tile_m) * cdiv(N, c[i].v.tile_n);
-    const double t = (double)cdiv(tiles, kCUs) * c[i].v.tile_m * c[i].v.tile_n /
-                     c[i].tflops;
+    const double t = estimate(c[i], M, N);
     if (i == 0 || t < best_t * 0.995) {
       best = i;
       best_t = t;
@@ -176,7 +196,6 @@ void set_name(sgemm_plan& p, const char* base, bool va, bool vb) {
 }
 
 // Chooses the kernel and fills the launch geometry for checked arguments.
-// algo must be valid; SGEMM_ALGO_MFMA_DIRECT must have 128-bit A and B.
 Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
               const float* B, int64_t ldb, const float* C, int64_t ldc,
               int algo) {
@@ -186,8 +205,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   const bool va = K == 0 || vec_a_ok(A, lda, K);
   const bool vb = K == 0 || vec_b_ok(B, ldb, N);
   const bool vc = aligned16(C) && ldc % 4 == 0 && N % 4 == 0;
-  if (algo == SGEMM_ALGO_AUTO)
-    algo = (va && vb) ? SGEMM_ALGO_MFMA_DIRECT : SGEMM_ALGO_MFMA;
+  if (algo == SGEMM_ALGO_AUTO) algo = SGEMM_ALGO_MFMA_DIRECT;
   p.info.algo = algo;
   p.info.vec_a = va;
   p.info.vec_b = vb;
@@ -281,9 +299,7 @@ const char* sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "success";
     case SGEMM_ERR_INVALID_ARG: return "invalid argument";
-    case SGEMM_ERR_UNSUPPORTED:
-      return "unsupported: an operand spans 2 GiB or more, or the LDS-direct "
-             "family was asked for rows that are not 128-bit aligned";
+    case SGEMM_ERR_UNSUPPORTED: return "unsupported: an operand spans 2 GiB or more";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
