@@ -1,0 +1,102 @@
+"""Static count of LDS traffic in the built kernels' main loops (CPU only).
+
+The pages count shared-memory loads per FMA: 2 for the one-output-per-thread
+loop, (TM + TN) / (TM TN) for a TM x TN register tile ("CUDA in depth (4):
+accessing shared memory efficiently", sections on too many shared-memory
+reads and on going from 1x1 to 2x2).  Here the same count is read off the
+gfx950 assembly of this library: words moved by LDS reads and multiply-adds
+(or matrix instructions) issued in one trip of each kernel's K loop.
+"""
+from __future__ import annotations
+
+import re
+import shutil
+
+import pytest
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None,
+                                reason="needs hipcc to build the assembly")
+
+READ_WORDS = {"ds_read_b32": 1, "ds_read2_b32": 2, "ds_read2st64_b32": 2,
+              "ds_read_b64": 2, "ds_read2_b64": 4, "ds_read2st64_b64": 4,
+              "ds_read_b96": 3, "ds_read_b128": 4}
+
+
+@pytest.fixture(scope="module")
+def asm():
+    from tiled_fp32_gemm_amd import build
+    return open(build.build_asm()).read()
+
+
+def kernel_body(asm: str, *parts: str) -> str:
+    names = [n for n in re.findall(r"^(_ZN2sg\w+):", asm, re.M)
+             if all(p in n for p in parts)]
+    assert len(names) == 1, (parts, names)
+    start = asm.index(names[0] + ":")
+    return asm[start:asm.index(".Lfunc_end", start)]
+
+
+def main_loop(body: str) -> list[str]:
+    """Instructions of the blocks at depth 1 of the outermost loop."""
+    hdr = re.search(r"^(\.LBB\w+):\s*;\s*=>This (?:Inner )?Loop Header: Depth=1",
+                    body, re.M)
+    assert hdr, "no loop"
+    tag = hdr.group(1)[2:]  # ".LBB13_3" is "BB13_3" in the comments
+    insts, inside = [], False
+    for line in body.split("\n"):
+        if re.match(r"^(\.LBB\w+|; %bb\.\d+):", line):
+            inside = (line.startswith(hdr.group(1) + ":") or
+                      (f"in Loop: Header={tag} Depth=1" in line))
+            continue
+        s = line.strip()
+        if inside and s and not s.startswith((";", ".")):
+            insts.append(s.split()[0])
+    return insts
+
+
+def counts(insts: list[str]) -> dict:
+    return {
+        "words": sum(READ_WORDS.get(i, 0) for i in insts),
+        "mfma": sum(i.startswith("v_mfma_f32_32x32x2") for i in insts),
+        "fma": sum(i in ("v_fma_f32", "v_fmac_f32", "v_fmac_f32_e32",
+                         "v_fma_f32_e64") for i in insts),
+        "other_reads": sorted({i for i in insts
+                               if i.startswith("ds_read") and i not in READ_WORDS}),
+    }
+
+
+def test_simple_kernel_is_two_loads_per_fma(asm):
+    c = counts(main_loop(kernel_body(asm, "sgemm_simple_kernel")))
+    assert not c["other_reads"]
+    assert c["fma"] == 16                 # one output, 16 k per tile step
+    assert c["words"] / c["fma"] == 2.0   # the pages' 1x1 figure
+
+
+@pytest.mark.parametrize("flags", ["Lb1ELb1ELb1E", "Lb0ELb0ELb0E"])
+def test_fma_kernel_is_the_8x8_register_tile(asm, flags):
+    c = counts(main_loop(kernel_body(asm, "sgemm_fma_kernel", flags)))
+    assert not c["other_reads"]
+    assert c["fma"] == 16 * 64                   # 16 k x 8 x 8
+    assert c["words"] / c["fma"] == (8 + 8) / (8 * 8)
+
+
+# (template fragment, TA, TB, 16-deep sub-slabs per wave group per slab)
+DIRECT = [("Li256ELi256ELi64ELi64ELi32ELi2ELi1E", 2, 2, 2),
+          ("Li128ELi128ELi64ELi32ELi32ELi2ELi1E", 2, 1, 2),
+          ("Li64ELi128ELi32ELi64ELi32ELi2ELi2E", 1, 2, 1),
+          ("Li64ELi64ELi32ELi32ELi32ELi2ELi2E", 1, 1, 1),
+          ("Li32ELi64ELi32ELi32ELi32ELi2ELi2E", 1, 1, 1),
+          ("Li32ELi64ELi32ELi32ELi64ELi2ELi4E", 1, 1, 1)]
+
+
+@pytest.mark.parametrize("frag,ta,tb,subs", DIRECT, ids=[d[0] for d in DIRECT])
+def test_direct_kernel_lds_traffic(asm, frag, ta, tb, subs):
+    c = counts(main_loop(kernel_body(asm, "sgemm_mfma_direct_kernel", frag)))
+    assert not c["other_reads"]
+    # per 16-deep sub-slab: 8 steps of TA x TB matrix instructions, fed by
+    # two 128-bit A reads per 32-row block and eight B words per 32 columns
+    assert c["mfma"] == subs * 8 * ta * tb
+    assert c["words"] == subs * 8 * (ta + tb)
+    # LDS bytes per flop of the wave: 64 lanes x 4 B per word over 4096
+    # flops per 32x32x2 instruction
+    assert c["words"] * 4 * 64 / (c["mfma"] * 4096) == (ta + tb) / (16 * ta * tb)
