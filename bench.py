@@ -17,7 +17,8 @@ is enqueued on.  Prints one JSON line.
   cpu_baseline     the CPU oracle on a bounded row sample of the same product
 
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
-the counter scale factors) and prints its size.
+the counter scale factors) and prints its size.  ``--op transpose`` measures
+the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s).
 """
 from __future__ import annotations
 
@@ -95,6 +96,59 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def bench_transpose(args) -> int:
+    """out = in^T on a rows x cols matrix: bytes moved = 2 * 4 * rows * cols."""
+    import numpy as np
+    import torch
+
+    import tiled_fp32_gemm_amd as sg
+    sg.load()
+    rows, cols = args.rows, args.cols
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    tin = torch.rand((rows, cols), device=dev, generator=g)
+    tout = torch.empty((cols, rows), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = sg.TRANSPOSE_LAYOUTS[args.layout]
+
+    def step():
+        st = sg.sgemm_transpose_ex(rows, cols, tin.data_ptr(), cols,
+                                   tout.data_ptr(), rows, stream.cuda_stream, code)
+        if st != sg.OK:
+            raise sg.SgemmError(st, "sgemm_transpose_ex")
+
+    for _ in range(args.warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    nbytes = 2.0 * 4 * rows * cols
+    achieved = nbytes / (float(ev_ms.mean()) / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "tiled transpose GB/s (fp32, 1 GPU)",
+        "value": round(nbytes * args.steps / wall / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"transpose {rows}x{cols} fp32, layout {args.layout}",
+                   "kernel_ms_median": round(float(np.median(ev_ms)), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -107,6 +161,11 @@ def main() -> int:
                     help="rows of the product the CPU oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--op", default="sgemm", choices=["sgemm", "transpose"])
+    ap.add_argument("--layout", default="auto",
+                    choices=["auto", "naive", "padded", "swizzled"])
+    ap.add_argument("--rows", type=int, default=8192)
+    ap.add_argument("--cols", type=int, default=8192)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,6 +183,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return 0
+    if args.op == "transpose":
+        return bench_transpose(args)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)

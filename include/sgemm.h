@@ -137,6 +137,43 @@ int sgemm_plan_query(int64_t M, int64_t N, int64_t K,
                      const float *C, int64_t ldc,
                      int algo, sgemm_plan *plan);
 
+/* out = in^T: in is rows x cols (row i at in + i*ldi, ldi >= max(1, cols)),
+ * out is cols x rows (row j at out + j*ldo, ldo >= max(1, rows)); out[j][i]
+ * = in[i][j], bit for bit.  This is the pages' tiled transpose ("Memory-bank
+ * mechanism and accelerated compute", section on the transpose kernel):
+ * coalesced row reads and row writes, with the column access done inside a
+ * 64 x 64 LDS tile.  Device pointers owned by the caller, 4-byte aligned, not
+ * overlapping; any leading dimension; enqueued on stream without
+ * synchronising.  Errors as for sgemm (checked before any HIP call);
+ * rows == 0 or cols == 0 is a no-op. */
+int sgemm_transpose(int64_t rows, int64_t cols,
+                    const float *in, int64_t ldi,
+                    float *out, int64_t ldo,
+                    hipStream_t stream);
+
+/* LDS tile layouts for sgemm_transpose_ex (all give the same result).  The
+ * tile is kept as 16-byte units and every LDS access is 128 bits wide; the
+ * column-wise reads of 4 x 4 blocks are where the layouts differ:
+ *   NAIVE     64 x 16 units, the unpadded control: the 16 lanes served
+ *             together read one 16-byte bank group (16-way conflicts).
+ *   PADDED    64 x 17 units, one extra unit per row, the pages' extra column
+ *             at the access width ("Memory-bank mechanism and accelerated
+ *             compute", section 'one extra column'): 4-way conflicts remain.
+ *   SWIZZLED  64 x 16 units, unit c of row r stored at c ^ ((r / 4) % 16)
+ *             (same page, section on alternatives to padding):
+ *             conflict-free; AUTO uses it. */
+#define SGEMM_TRANSPOSE_AUTO 0
+#define SGEMM_TRANSPOSE_NAIVE 1
+#define SGEMM_TRANSPOSE_PADDED 2
+#define SGEMM_TRANSPOSE_SWIZZLED 3
+
+/* As sgemm_transpose with an explicit LDS layout; an unknown layout is
+ * SGEMM_ERR_INVALID_ARG. */
+int sgemm_transpose_ex(int64_t rows, int64_t cols,
+                       const float *in, int64_t ldi,
+                       float *out, int64_t ldo,
+                       hipStream_t stream, int layout);
+
 /* Static English text for a status code (never NULL). */
 const char *sgemm_status_string(int status);
 

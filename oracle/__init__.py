@@ -21,7 +21,7 @@ import numpy as np
 
 from . import build as _build
 
-__all__ = ["gemm", "max_threads", "library_path", "load_library"]
+__all__ = ["gemm", "transpose", "max_threads", "library_path", "load_library"]
 
 _lib = None
 
@@ -34,6 +34,8 @@ def load_library(path: str):
     lib.oracle_gemm_f64.argtypes = [i64, i64, i64, fp, i64, fp, i64,
                                     fp, i64, fp, i64, ctypes.c_int]
     lib.oracle_gemm_f64.restype = ctypes.c_int
+    lib.oracle_transpose_f32.argtypes = [i64, i64, fp, i64, fp, i64]
+    lib.oracle_transpose_f32.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -90,3 +92,21 @@ def gemm(A: np.ndarray, B: np.ndarray, M: int | None = None,
     if rc != 0:
         raise ValueError(f"oracle_gemm_f64 rejected the arguments (rc={rc})")
     return C, T
+
+
+def transpose(A: np.ndarray, rows: int | None = None, cols: int | None = None,
+              ldo: int | None = None, fill: float = np.nan, lib=None) -> np.ndarray:
+    """The ``cols x ldo`` float32 array whose first ``rows`` columns hold
+    ``A[:rows, :cols]`` transposed; the gap columns keep ``fill``."""
+    A = _rowmajor(A, "A")
+    rows = A.shape[0] if rows is None else rows
+    cols = A.shape[1] if cols is None else cols
+    ldo = max(rows, 1) if ldo is None else ldo
+    ldi = A.strides[0] // 4 if A.shape[0] > 1 else max(A.shape[1], 1)
+    out = np.full((cols, ldo), fill, dtype=np.float32)
+    lib = _load() if lib is None else lib
+    rc = lib.oracle_transpose_f32(rows, cols, A.ctypes.data, max(ldi, cols, 1),
+                                  out.ctypes.data, ldo)
+    if rc != 0:
+        raise ValueError(f"oracle_transpose_f32 rejected the arguments (rc={rc})")
+    return out

@@ -28,6 +28,10 @@
  *
  * Degenerate shapes: K == 0 gives C = T = 0 (the empty sum); M == 0 or N == 0
  * touches nothing.
+ *
+ * The file also holds the reference for the pages' tiled transpose kernel
+ * ("Memory-bank mechanism and accelerated compute", section on the transpose
+ * kernel): out[j][i] = in[i][j], a plain double loop.
  */
 #include <math.h>
 #include <stddef.h>
@@ -89,5 +93,22 @@ int oracle_gemm_f64(int64_t M, int64_t N, int64_t K,
             }
         }
     }
+    return 0;
+}
+
+/*
+ * out (cols x rows, leading dimension ldo) = in^T, in being rows x cols with
+ * leading dimension ldi: out[j*ldo + i] = in[i*ldi + j].  Gap columns of out
+ * are not written.  Returns 0, or -1 on a negative size or a leading
+ * dimension smaller than its row.
+ */
+int oracle_transpose_f32(int64_t rows, int64_t cols,
+                         const float *in, int64_t ldi,
+                         float *out, int64_t ldo)
+{
+    if (rows < 0 || cols < 0 || ldi < cols || ldo < rows) return -1;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j)
+            out[j * ldo + i] = in[i * ldi + j];
     return 0;
 }

@@ -151,3 +151,38 @@ def pin_empty(gemm) -> None:
 
 ALL_PINS = [pin_identity, pin_all_ones, pin_closed_forms, pin_brute_force,
             pin_numpy, pin_leading_dims, pin_transpose, pin_empty]
+
+
+# -- the transpose reference ------------------------------------------------
+# Each takes ``tr(A, **kw) -> out`` with the signature of oracle.transpose.
+
+def pin_transpose_numpy(tr) -> None:
+    """Agreement, bit for bit, with numpy's transposed view on many shapes."""
+    for (r, c, seed) in [(1, 1, 1), (1, 7, 2), (7, 1, 3), (13, 29, 4),
+                         (64, 64, 5), (65, 63, 6), (200, 3, 7)]:
+        A = seedgen.matrix(r, c, "normal", seed)
+        assert np.array_equal(tr(A), np.ascontiguousarray(A.T))
+
+
+def pin_transpose_index_form(tr) -> None:
+    """in[i][j] = i * cols + j (exact integers) lands at out[j][i]."""
+    r, c = 37, 53
+    A = (np.arange(r)[:, None] * c + np.arange(c)[None, :]).astype(np.float32)
+    out = tr(A)
+    for j in range(c):
+        for i in range(r):
+            assert out[j, i] == i * c + j
+
+
+def pin_transpose_leading_dims(tr) -> None:
+    """Input gaps (NaN) are not read; output gaps keep their fill."""
+    r, c = 9, 14
+    A = seedgen.matrix(r, c, "uniform", 8, ld=c + 5, fill=np.nan)
+    out = tr(A[:, :c], rows=r, cols=c, ldo=r + 3, fill=-5.0)
+    assert out.shape == (c, r + 3)
+    assert np.array_equal(out[:, :r], np.ascontiguousarray(A[:, :c].T))
+    assert np.all(out[:, r:] == -5.0)
+
+
+TRANSPOSE_PINS = [pin_transpose_numpy, pin_transpose_index_form,
+                  pin_transpose_leading_dims]

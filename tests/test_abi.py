@@ -147,3 +147,24 @@ def test_plans_per_family(lib):
         st, plan = call(300, 200, 100, lda=100, algo=sg.ALGOS[name])
         assert st == sg.OK and plan.kernel.decode().startswith(prefix)
         assert plan.lds_bytes <= 160 * 1024
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(rows=-1, cols=4), sg.ERR_INVALID_ARG),
+    (dict(rows=4, cols=8, ldi=7), sg.ERR_INVALID_ARG),       # ldi < cols
+    (dict(rows=8, cols=4, ldo=7), sg.ERR_INVALID_ARG),       # ldo < rows
+    (dict(rows=4, cols=4, inp=0), sg.ERR_INVALID_ARG),
+    (dict(rows=4, cols=4, out=BIG + 2), sg.ERR_INVALID_ARG),
+    (dict(rows=4, cols=4, out=BIG + 32), sg.ERR_INVALID_ARG),  # overlap
+    (dict(rows=4, cols=4, layout=4), sg.ERR_INVALID_ARG),
+    (dict(rows=1 << 16, cols=1 << 13), sg.ERR_UNSUPPORTED),  # 2 GiB
+    (dict(rows=0, cols=4, inp=0, out=0), sg.OK),
+])
+def test_transpose_checks(lib, args, status):
+    rows, cols = args["rows"], args["cols"]
+    inp = args.get("inp", BIG)
+    out = args.get("out", BIG + (1 << 32))
+    ldi = args.get("ldi", max(cols, 1))
+    ldo = args.get("ldo", max(rows, 1))
+    assert sg.sgemm_transpose_ex(rows, cols, inp, ldi, out, ldo, 0,
+                                 args.get("layout", 0)) == status

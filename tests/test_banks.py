@@ -115,3 +115,16 @@ def test_model_catches_a_bad_layout():
     # and B read halves 8 rows apart with an unpadded 128-float pitch: 2-way
     acc = [[4 * ((8 * (l >> 5)) * 128 + (l & 31))] for l in range(64)]
     assert banks.conflict_degree(acc, banks.GFX950_BANKS) == 2
+
+
+def test_transpose_gather_naive_and_padded_conflict():
+    # the unpadded control: the 16 lanes of a 128-bit read share one bank
+    # group; one extra unit per row leaves 4 distinct groups (4-way)
+    for e in range(4):
+        for w in range(4):
+            assert banks.conflict_degree(banks.transpose_gather("naive", e=e, wave=w),
+                                         banks.GFX950_BANKS) == 16
+            assert banks.conflict_degree(banks.transpose_gather("padded", e=e, wave=w),
+                                         banks.GFX950_BANKS) == 4
+            assert banks.conflict_degree(banks.transpose_gather("swizzled", e=e, wave=w),
+                                         banks.GFX950_BANKS) == 1

@@ -11,7 +11,7 @@ import oracle
 import seedgen
 from oracle import build as oracle_build
 
-from oracle_pins import ALL_PINS
+from oracle_pins import ALL_PINS, TRANSPOSE_PINS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -84,5 +84,39 @@ def test_pins_catch_planted_mistake(tmp_path, name):
         try:
             pin(gemm)
         except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
+
+
+@pytest.mark.parametrize("pin", TRANSPOSE_PINS, ids=lambda p: p.__name__)
+def test_transpose_pin(oracle_mod, pin):
+    pin(oracle_mod.transpose)
+
+
+TRANSPOSE_MUTANTS = {
+    "no_transpose": ("out[j * ldo + i] = in[i * ldi + j];",
+                     "out[i * ldo + j] = in[i * ldi + j];"),
+    "input_stride": ("out[j * ldo + i] = in[i * ldi + j];",
+                     "out[j * ldo + i] = in[i * cols + j];"),
+    "last_row_dropped": ("for (int64_t i = 0; i < rows; ++i)\n        for (int64_t j = 0; j < cols; ++j)",
+                         "for (int64_t i = 0; i + 1 < rows; ++i)\n        for (int64_t j = 0; j < cols; ++j)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TRANSPOSE_MUTANTS))
+def test_transpose_pins_catch_planted_mistake(tmp_path, name):
+    old, new = TRANSPOSE_MUTANTS[name]
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    path = tmp_path / f"oracle_{name}.c"
+    path.write_text(src.replace(old, new, 1))
+    so = str(tmp_path / f"liboracle_{name}.so")
+    oracle_build.compile_source(str(path), so)
+    lib = oracle.load_library(so)
+    failed = []
+    for pin in TRANSPOSE_PINS:
+        try:
+            pin(lambda A, **kw: oracle.transpose(A, lib=lib, **kw))
+        except (AssertionError, ValueError, IndexError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught mutant {name}"

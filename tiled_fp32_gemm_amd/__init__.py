@@ -23,12 +23,15 @@ import os
 __all__ = ["sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_status_string",
            "sgemm_version", "matmul", "library_path", "load", "SgemmPlan",
            "SgemmError", "ALGOS", "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED",
-           "ERR_LAUNCH", "EXPORTED_SYMBOLS"]
+           "ERR_LAUNCH", "EXPORTED_SYMBOLS", "sgemm_transpose",
+           "sgemm_transpose_ex", "transpose", "TRANSPOSE_LAYOUTS"]
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
 ALGOS = {"auto": 0, "simple": 1, "fma": 2, "mfma": 3, "mfma_direct": 4}
 EXPORTED_SYMBOLS = ("sgemm", "sgemm_ex", "sgemm_plan_query",
+                    "sgemm_transpose", "sgemm_transpose_ex",
                     "sgemm_status_string", "sgemm_version")
+TRANSPOSE_LAYOUTS = {"auto": 0, "naive": 1, "padded": 2, "swizzled": 3}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsgemm.so")
@@ -78,6 +81,11 @@ def load():
     lib.sgemm_ex.restype = i32
     lib.sgemm_plan_query.argtypes = common + [i32, ctypes.POINTER(SgemmPlan)]
     lib.sgemm_plan_query.restype = i32
+    tr = [i64, i64, fp, i64, fp, i64, fp]
+    lib.sgemm_transpose.argtypes = tr
+    lib.sgemm_transpose.restype = i32
+    lib.sgemm_transpose_ex.argtypes = tr + [i32]
+    lib.sgemm_transpose_ex.restype = i32
     lib.sgemm_status_string.argtypes = [i32]
     lib.sgemm_status_string.restype = ctypes.c_char_p
     lib.sgemm_version.argtypes = []
@@ -102,6 +110,36 @@ def sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, algo=0):
     st = load().sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, algo,
                                  ctypes.byref(plan))
     return st, plan
+
+
+def sgemm_transpose(rows, cols, inp, ldi, out, ldo, stream=0) -> int:
+    """out = inp^T (rows x cols -> cols x rows); returns the status code."""
+    return load().sgemm_transpose(rows, cols, inp, ldi, out, ldo, stream)
+
+
+def sgemm_transpose_ex(rows, cols, inp, ldi, out, ldo, stream=0, layout=0) -> int:
+    """``sgemm_transpose`` with an explicit LDS layout (``TRANSPOSE_LAYOUTS``)."""
+    return load().sgemm_transpose_ex(rows, cols, inp, ldi, out, ldo, stream,
+                                     layout)
+
+
+def transpose(A, out=None, layout: str | int = "auto", stream=None):
+    """``out = A.T`` for a float32 GPU tensor (row-major, any row stride)."""
+    import torch
+    if A.dtype != torch.float32 or A.device.type != "cuda" or A.dim() != 2:
+        raise ValueError("A must be a 2-D float32 GPU tensor")
+    rows, cols = A.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != (cols, rows) or out.dtype != torch.float32:
+        raise ValueError("out must be a float32 tensor of shape A.T")
+    code = TRANSPOSE_LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    s = torch.cuda.current_stream(A.device) if stream is None else stream
+    st = sgemm_transpose_ex(rows, cols, A.data_ptr(), _ld(A, "A"),
+                            out.data_ptr(), _ld(out, "out"), s.cuda_stream, code)
+    if st != OK:
+        raise SgemmError(st, "sgemm_transpose_ex")
+    return out
 
 
 def sgemm_status_string(status: int) -> str:

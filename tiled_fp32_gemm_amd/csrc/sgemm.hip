@@ -10,6 +10,7 @@
 #include "kernel_mfma.hpp"
 #include "kernel_mfma_direct.hpp"
 #include "kernel_simple.hpp"
+#include "kernel_transpose.hpp"
 
 namespace {
 
@@ -68,6 +69,7 @@ int check(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 typedef void (*KernelFn)(GemmArgs);
+typedef void (*KernelFnT)(sg::TransposeArgs);
 
 struct Plan {
   sgemm_plan info;
@@ -293,6 +295,58 @@ int sgemm_plan_query(int64_t M, int64_t N, int64_t K, const float* A,
   if (st != SGEMM_OK) return st;
   *plan = plan_for(M, N, K, A, lda, B, ldb, C, ldc, algo).info;
   return SGEMM_OK;
+}
+
+int sgemm_transpose_ex(int64_t rows, int64_t cols, const float* in,
+                       int64_t ldi, float* out, int64_t ldo,
+                       hipStream_t stream, int layout) {
+  if (layout < SGEMM_TRANSPOSE_AUTO || layout > SGEMM_TRANSPOSE_SWIZZLED)
+    return SGEMM_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0) return SGEMM_ERR_INVALID_ARG;
+  if (ldi < (cols > 1 ? cols : 1) || ldo < (rows > 1 ? rows : 1))
+    return SGEMM_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return SGEMM_OK;
+  const int64_t ib = span_bytes(rows, cols, ldi), ob = span_bytes(cols, rows, ldo);
+  if (in == nullptr || out == nullptr || ((uintptr_t)in & 3u) || ((uintptr_t)out & 3u))
+    return SGEMM_ERR_INVALID_ARG;
+  if (ib < 0 || ob < 0 || ib >= kMaxOperandBytes || ob >= kMaxOperandBytes)
+    return SGEMM_ERR_UNSUPPORTED;
+  if (overlaps(in, ib, out, ob)) return SGEMM_ERR_INVALID_ARG;
+
+  sg::TransposeArgs a;
+  a.in = in;
+  a.out = out;
+  a.in_bytes = (uint32_t)ib;
+  a.out_bytes = (uint32_t)ob;
+  a.rows = (int)rows;
+  a.cols = (int)cols;
+  a.ldi = (int)(rows > 1 ? ldi : (cols > 1 ? cols : 1));
+  a.ldo = (int)(cols > 1 ? ldo : (rows > 1 ? rows : 1));
+  a.tiles_x = (int)cdiv(cols, 64);
+  const int64_t tiles = cdiv(cols, 64) * cdiv(rows, 64);
+  const bool vi = aligned16(in) && a.ldi % 4 == 0 && cols % 4 == 0;
+  const bool vo = aligned16(out) && a.ldo % 4 == 0 && rows % 4 == 0;
+  if (layout == SGEMM_TRANSPOSE_AUTO) layout = SGEMM_TRANSPOSE_SWIZZLED;
+  static const KernelFnT table[3][4] = {
+#define SG_T(L) {sg::sgemm_transpose_kernel<L, false, false>,   \
+                 sg::sgemm_transpose_kernel<L, false, true>,    \
+                 sg::sgemm_transpose_kernel<L, true, false>,    \
+                 sg::sgemm_transpose_kernel<L, true, true>}
+      SG_T(sg::kNaive), SG_T(sg::kPadded), SG_T(sg::kSwizzled)
+#undef SG_T
+  };
+  const KernelFnT fn = table[layout - 1][(vi ? 2 : 0) | (vo ? 1 : 0)];
+  void* kargs[] = {&a};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
+                                       dim3((unsigned)tiles), dim3(256), kargs,
+                                       0, stream);
+  return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int sgemm_transpose(int64_t rows, int64_t cols, const float* in, int64_t ldi,
+                    float* out, int64_t ldo, hipStream_t stream) {
+  return sgemm_transpose_ex(rows, cols, in, ldi, out, ldo, stream,
+                            SGEMM_TRANSPOSE_AUTO);
 }
 
 const char* sgemm_status_string(int status) {
