@@ -93,9 +93,11 @@ def test_transpose_pin(oracle_mod, pin):
     pin(oracle_mod.transpose)
 
 
+# Every mutant keeps its accesses inside the buffers the wrapper allocates, so
+# that a planted mistake fails a pin instead of corrupting the test process.
 TRANSPOSE_MUTANTS = {
-    "no_transpose": ("out[j * ldo + i] = in[i * ldi + j];",
-                     "out[i * ldo + j] = in[i * ldi + j];"),
+    "output_stride": ("out[j * ldo + i] = in[i * ldi + j];",
+                      "out[j * rows + i] = in[i * ldi + j];"),
     "input_stride": ("out[j * ldo + i] = in[i * ldi + j];",
                      "out[j * ldo + i] = in[i * cols + j];"),
     "last_row_dropped": ("for (int64_t i = 0; i < rows; ++i)\n        for (int64_t j = 0; j < cols; ++j)",
