@@ -14,7 +14,8 @@ is enqueued on.  Prints one JSON line.
                    WRITE_SIZE counters recorded under profiles/, each scaled
                    by the factor a plain copy of known size gives, or null
                    when the kernel sources changed since they were taken
-  cpu_baseline     the CPU oracle on a bounded row sample of the same product
+  cpu_baseline     the CPU oracle on a bounded row sample of the same product,
+                   repeated for about --cpu-seconds
 
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
 the counter scale factors) and prints its size.  ``--op transpose`` measures
@@ -76,18 +77,24 @@ def read_traffic(kernel: str, workload: str, src_hash: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(A, B, M, N, K, rows: int) -> dict:
+def cpu_baseline(A, B, M, N, K, rows: int, seconds: float) -> dict:
+    """The oracle on rows 0..rows-1 of the product, repeated until `seconds`
+    of CPU time have passed (at least once, at most 50 times)."""
     import oracle
     rows = min(rows, M)
     sub = A[:rows]
     oracle.gemm(sub[:8], B, with_t=False)           # load + warm the library
-    t0 = time.perf_counter()
-    oracle.gemm(sub, B, with_t=False)
-    dt = time.perf_counter() - t0
-    return {"value": round(2.0 * rows * N * K / dt / 1e12, 6),
+    reps, total = 0, 0.0
+    while reps < 50 and (reps == 0 or total < seconds):
+        t0 = time.perf_counter()
+        oracle.gemm(sub, B, with_t=False)
+        total += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(2.0 * rows * N * K * reps / total / 1e12, 6),
             "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product "
-                      f"(C only, fp64 accumulation), {dt:.2f} s"}
+                      f"(C only, fp64 accumulation), {reps} run(s) in "
+                      f"{total:.2f} s"}
 
 
 def copy_calibration(nbytes: int) -> None:
@@ -164,6 +171,8 @@ def main() -> int:
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "simple"])
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the product the CPU oracle computes")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle sample until this much time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--op", default="sgemm", choices=["sgemm", "transpose"])
@@ -276,7 +285,8 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_rows,
+                                           args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 

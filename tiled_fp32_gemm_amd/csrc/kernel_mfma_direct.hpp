@@ -43,7 +43,13 @@
 // Pipeline with S stages: up to S - 1 slabs are in flight while slab t is
 // computed; at the top of each step a wave waits until its own loads of slab
 // t have landed, then one barrier makes every wave's loads visible and frees
-// the stage of slab t-1 for slab t + S - 1.
+// the stage of slab t-1 for slab t + S - 1.  A wave's loads of that slab are
+// not issued in one burst after the barrier but one at a time between the
+// matrix instructions of its first sub-slab: issued together, the loads of
+// all waves land in LDS at the same moment and hold up the fragment reads
+// (measured on MI355X: 142.3 -> 144.7 TFLOP/s at 4096^3 for the 256 x 256
+// tile, +2% for 128 x 128).  Split-K variants issue them at once: their
+// slabs are short, and a later issue costs them more than the burst.
 //
 // Split K inside the workgroup (KS > 1, for shapes with too few tiles to fill
 // the chip): KS wave groups compute the same tile over their own sub-slabs
@@ -162,22 +168,34 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
     b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u;
   }
 
-  // Issue the direct loads of the slab starting at k0 into stage st.  A group
-  // is loaded when its first element is inside the matrix.
-  auto issue = [&](int k0, int st) {
+  // Issue direct load l (the A slots, then the B slots) of the slab starting
+  // at k0 into stage st.  A group is loaded when its first element is inside
+  // the matrix.
+  auto issue_one = [&](int l, int k0, int st) {
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
+      if (l != s) continue;
       float* dst = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave);
       const bool ok = a_row_ok[s] && (k0 + a_k[s]) < g.K;
       load4_to_lds(ra, dst, ok ? a_off[s] + (uint32_t)k0 * 4u : kOob);
     }
 #pragma unroll
     for (int s = 0; s < Cfg::B_SLOTS; ++s) {
+      if (l != Cfg::A_SLOTS + s) continue;
       float* dst = Bs + st * Cfg::B_STAGE + 4 * (s * NT + 64 * wave);
       const bool ok = b_col_ok[s] && (k0 + b_k[s]) < g.K;
       load4_to_lds(rb, dst, ok ? b_off[s] + (uint32_t)k0 * (uint32_t)g.ldb * 4u : kOob);
     }
   };
+  auto issue = [&](int k0, int st) {
+#pragma unroll
+    for (int l = 0; l < Cfg::LOADS; ++l) issue_one(l, k0, st);
+  };
+
+  // Spread the loads only where a slab's compute is long (one wave group):
+  // with split K a slab lasts a few hundred cycles per wave, and issuing its
+  // successor's loads any later costs more than the burst does.
+  constexpr bool kSpread = KS == 1;
 
   f32x16 acc[TA][TB];
 #pragma unroll
@@ -214,8 +232,9 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
     // moving LDS accesses across it.  (A full __syncthreads() fence would
     // also wait for the later slabs, which must stay in flight.)
     asm volatile("s_barrier" ::: "memory");
-    if (t + DEPTH < nslab)
-      issue((t + DEPTH) * BK, st == 0 ? STAGES - 1 : st - 1);
+    const bool more = t + DEPTH < nslab;
+    const int nk0 = (t + DEPTH) * BK, nst = st == 0 ? STAGES - 1 : st - 1;
+    if (!kSpread && more) issue(nk0, nst);
 
     const float* as = As + st * Cfg::A_STAGE;
     const float* bs = Bs + st * Cfg::B_STAGE;
@@ -242,13 +261,21 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
         }
       }
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
+      for (int p = 0; p < 8; ++p) {
+        // Load l of the next slab goes before step l * 8 / LOADS of the
+        // first sub-slab (whole-slab wave groups only; see the top).
+        if (kSpread && uu == 0) {
+#pragma unroll
+          for (int l = 0; l < Cfg::LOADS; ++l)
+            if (p == l * 8 / Cfg::LOADS && more) issue_one(l, nk0, nst);
+        }
 #pragma unroll
         for (int i = 0; i < TA; ++i)
 #pragma unroll
           for (int j = 0; j < TB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                 af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
+      }
     }
     st = (st == STAGES - 1) ? 0 : st + 1;
   }

@@ -128,12 +128,12 @@ const Candidate* mfma_candidates(bool direct, int& n) {
   // barriers per flop against 16-deep slabs in three stages.  "ks" names the
   // number of wave groups that split each slab.
   static const Candidate lds[6] = {
-      {direct_variant<256, 256, 64, 64, 32, 2, 1>("mfma_lds_256x256x32"), 143.1},
-      {direct_variant<128, 128, 64, 32, 32, 2, 1>("mfma_lds_128x128x32"), 138.1},
-      {direct_variant<64, 128, 32, 64, 32, 2, 2>("mfma_lds_64x128x32_ks2"), 137.5},
-      {direct_variant<64, 64, 32, 32, 32, 2, 2>("mfma_lds_64x64x32_ks2"), 133.4},
-      {direct_variant<32, 64, 32, 32, 32, 2, 2>("mfma_lds_32x64x32_ks2"), 124.9},
-      {direct_variant<32, 64, 32, 32, 64, 2, 4>("mfma_lds_32x64x64_ks4"), 122.4}};
+      {direct_variant<256, 256, 64, 64, 32, 2, 1>("mfma_lds_256x256x32"), 144.7},
+      {direct_variant<128, 128, 64, 32, 32, 2, 1>("mfma_lds_128x128x32"), 141.1},
+      {direct_variant<64, 128, 32, 64, 32, 2, 2>("mfma_lds_64x128x32_ks2"), 136.2},
+      {direct_variant<64, 64, 32, 32, 32, 2, 2>("mfma_lds_64x64x32_ks2"), 135.2},
+      {direct_variant<32, 64, 32, 32, 32, 2, 2>("mfma_lds_32x64x32_ks2"), 127.4},
+      {direct_variant<32, 64, 32, 32, 64, 2, 4>("mfma_lds_32x64x64_ks4"), 125.0}};
   n = direct ? 6 : 3;
   return direct ? lds : reg;
 }
