@@ -69,7 +69,7 @@ typedef struct ihipStream_t *hipStream_t;
 extern "C" {
 #endif
 
-#define SGEMM_VERSION 100 /* 1.0.0 */
+#define SGEMM_VERSION 110 /* 1.1.0 */
 
 /* Status codes. */
 #define SGEMM_OK 0
@@ -119,7 +119,10 @@ int sgemm_ex(int64_t M, int64_t N, int64_t K,
 
 /* What a call with these arguments would launch, without launching it.  The
  * checks and return codes are those of sgemm_ex; on SGEMM_OK *plan is filled
- * (kernel name, workgroup tile, grid).  plan must not be NULL. */
+ * (kernel name, workgroup tile, grid).  plan must not be NULL.  AUTO picks
+ * the LDS-direct tile (and K split) with the least estimated time for
+ * M x N x K: wave quantisation over the 256 CUs, resident workgroups per CU,
+ * slab load latency and the final C stores, with rates measured on MI355X. */
 typedef struct sgemm_plan {
     int algo;            /* family actually used (AUTO resolved) */
     int tile_m, tile_n;  /* C tile per workgroup */
@@ -128,6 +131,8 @@ typedef struct sgemm_plan {
     int vec_a, vec_b;    /* 1 if A / B rows take 128-bit loads */
     int64_t workgroups;  /* grid size (0 when nothing is launched) */
     int lds_bytes;       /* LDS per workgroup */
+    int wg_per_cu;       /* workgroups one CU holds at once (LDS and
+                            registers of the kernel as built for gfx950) */
     char kernel[64];     /* kernel name, NUL-terminated */
 } sgemm_plan;
 

@@ -44,7 +44,7 @@ def test_one_hip_runtime_is_mapped(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert sg.sgemm_version() == 100
+    assert sg.sgemm_version() == 110
     assert sg.sgemm_status_string(sg.OK) == "success"
     for st in (sg.ERR_INVALID_ARG, sg.ERR_UNSUPPORTED, sg.ERR_LAUNCH):
         assert sg.sgemm_status_string(st) not in ("", "success")
@@ -121,9 +121,9 @@ def test_k_zero_plans_a_zero_fill(lib, algo):
     (256, 256, 256, 256, 256, 4, "mfma_lds_32x64x64_ks4_savb", 32),  # A 4B-aligned
     (256, 256, 256, 258, 256, 0, "mfma_lds_32x64x64_ks4_savb", 32),  # lda % 4 != 0
     (4096, 4096, 4095, 4095, 4096, 0, "mfma_lds_256x256x32_savb", 256),
-    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x32_ks2_vavb", 2209),
-    (2048, 2048, 2048, 2048, 2048, 0, "mfma_lds_128x128x32_vavb", 256),
-    (512, 4096, 4096, 4096, 4096, 0, "mfma_lds_64x128x32_ks2_vavb", 256),
+    (3000, 3000, 512, 512, 3000, 0, "mfma_lds_64x64x32_vavb", 2209),
+    (2048, 2048, 2048, 2048, 2048, 0, "mfma_lds_64x128x32_vavb", 512),
+    (512, 4096, 4096, 4096, 4096, 0, "mfma_lds_64x64x32_vavb", 512),
     (384, 4096, 64, 64, 4096, 0, "mfma_lds_32x64x32_ks2_vavb", 768),
 ])
 def test_plans(lib, M, N, K, lda, ldb, aoff, kernel, wgs):

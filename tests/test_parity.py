@@ -237,9 +237,11 @@ def test_largest_operand(K):
 # pick), each with K not a multiple of 4 so that the straddling A groups are
 # zero-filled, and with an odd lda so that A rows are only 4-byte aligned.
 VARIANT_SHAPES = [
-    ("mfma_lds_256x256x32", 4096, 4096, 22),
-    ("mfma_lds_128x128x32", 1024, 4096, 38),
-    ("mfma_lds_64x128x32_ks2", 512, 4096, 45),
+    ("mfma_lds_256x256x32", 2048, 8192, 450),
+    ("mfma_lds_128x128x32", 4096, 4096, 22),
+    ("mfma_lds_64x128x32", 2048, 2048, 45),
+    ("mfma_lds_64x128x32_ks2", 640, 3072, 42),
+    ("mfma_lds_64x64x32", 1536, 3072, 47),
     ("mfma_lds_64x64x32_ks2", 3072, 192, 53),
     ("mfma_lds_32x64x32_ks2", 384, 4096, 61),
     ("mfma_lds_32x64x64_ks4", 32, 64, 67),

@@ -50,7 +50,8 @@ class SgemmPlan(ctypes.Structure):
                 ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("threads", ctypes.c_int), ("vec_a", ctypes.c_int),
                 ("vec_b", ctypes.c_int), ("workgroups", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int), ("kernel", ctypes.c_char * 64)]
+                ("lds_bytes", ctypes.c_int), ("wg_per_cu", ctypes.c_int),
+                ("kernel", ctypes.c_char * 64)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_}

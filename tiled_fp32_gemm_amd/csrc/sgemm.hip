@@ -109,77 +109,99 @@ Variant direct_variant(const char* name) {
   return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, f, f, f, f};
 }
 
-// Matrix-core configurations, large to small tiles, each with its
-// steady-state rate on MI355X in TFLOP/s (measured at M = N = K = 4096 with
-// the chip full).  The large tiles cut L2 traffic per flop; the small ones,
-// and those that split K over wave groups, keep more of the chip busy on
-// small or ragged shapes.
+// Matrix-core configurations, large to small tiles, with the planner's two
+// inputs for each:
+//   eff  the fraction of a CU's FP32 matrix peak the variant sustains with
+//        its pipes busy (fitted, with the constants below, to MI355X timings
+//        of every variant on 196 shapes from 96 to 65536 per side, chosen
+//        within 0.4% of the fastest variant on average);
+//   occ  the workgroups a CU holds at once, from the kernel's LDS bytes and
+//        its registers per lane (512 per SIMD lane, at most 8 waves per
+//        SIMD) as compiled for gfx950.
+// The large tiles cut L2 traffic per flop; the small ones, and those that
+// split K over wave groups, keep more of the chip busy on small, ragged or
+// short-K shapes.
 struct Candidate {
   Variant v;
-  double tflops;
+  double eff;
+  int occ;
 };
 
 const Candidate* mfma_candidates(bool direct, int& n) {
   static const Candidate reg[3] = {
-      {reg_variant<256, 128, 64, 64, 16>("mfma_256x128x16"), 139.0},
-      {reg_variant<128, 128, 64, 32, 16>("mfma_128x128x16"), 132.0},
-      {reg_variant<64, 64, 32, 32, 16>("mfma_64x64x16"), 125.0}};
+      {reg_variant<256, 128, 64, 64, 16>("mfma_256x128x16"), 0.86, 2},
+      {reg_variant<128, 128, 64, 32, 16>("mfma_128x128x16"), 0.81, 3},
+      {reg_variant<64, 64, 32, 32, 16>("mfma_64x64x16"), 0.77, 8}};
   // LDS-direct: 32-deep slabs in two stages (one slab in flight) halve the
   // barriers per flop against 16-deep slabs in three stages.  "ks" names the
   // number of wave groups that split each slab.
-  static const Candidate lds[6] = {
-      {direct_variant<256, 256, 64, 64, 32, 2, 1>("mfma_lds_256x256x32"), 144.7},
-      {direct_variant<128, 128, 64, 32, 32, 2, 1>("mfma_lds_128x128x32"), 141.1},
-      {direct_variant<64, 128, 32, 64, 32, 2, 2>("mfma_lds_64x128x32_ks2"), 136.2},
-      {direct_variant<64, 64, 32, 32, 32, 2, 2>("mfma_lds_64x64x32_ks2"), 135.2},
-      {direct_variant<32, 64, 32, 32, 32, 2, 2>("mfma_lds_32x64x32_ks2"), 127.4},
-      {direct_variant<32, 64, 32, 32, 64, 2, 4>("mfma_lds_32x64x64_ks4"), 125.0}};
-  n = direct ? 6 : 3;
+  static const Candidate lds[8] = {
+      {direct_variant<256, 256, 64, 64, 32, 2, 1>("mfma_lds_256x256x32"), 0.929, 1},
+      {direct_variant<128, 128, 64, 32, 32, 2, 1>("mfma_lds_128x128x32"), 0.868, 2},
+      {direct_variant<64, 128, 32, 64, 32, 2, 1>("mfma_lds_64x128x32"), 0.901, 3},
+      {direct_variant<64, 128, 32, 64, 32, 2, 2>("mfma_lds_64x128x32_ks2"), 0.805, 3},
+      {direct_variant<64, 64, 32, 32, 32, 2, 1>("mfma_lds_64x64x32"), 0.837, 5},
+      {direct_variant<64, 64, 32, 32, 32, 2, 2>("mfma_lds_64x64x32_ks2"), 0.830, 4},
+      {direct_variant<32, 64, 32, 32, 32, 2, 2>("mfma_lds_32x64x32_ks2"), 0.799, 6},
+      {direct_variant<32, 64, 32, 32, 64, 2, 4>("mfma_lds_32x64x64_ks4"), 0.807, 3}};
+  n = direct ? 8 : 3;
   return direct ? lds : reg;
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kCUs = 256;             // MI355X compute units
-constexpr int kLdsPerCU = 160 * 1024;  // bytes
-constexpr int kWavesPerCU = 16;        // at <= 128 VGPRs per lane
-constexpr double kSaturate = 2.0;      // waves per SIMD that keep MFMA busy
+constexpr int kCUs = 256;                      // MI355X compute units
+constexpr double kPeakPerCU = 157.3e12 / kCUs;  // FP32 matrix flop/s per CU
+constexpr double kSaturate = 1.28;   // waves per SIMD that keep the pipes busy
+constexpr double kSlabFloor = 0.61e-6;  // s: a slab's wait for its loads
+constexpr double kRoundCost = 4.4e-6;   // s: fill and drain of one round
+constexpr double kWriteBW = 4.52e12;    // B/s: C stores of a final round
 
-// Estimated time (arbitrary units) of variant v on an M x N product.
-// Workgroups are spread evenly over the CUs, so the busiest CU computes
-// n = ceil(tiles / CUs) tiles of BM x BN (charging partial-tile padding and
-// the idle CUs of the last round, i.e. wave quantisation).  Up to `occ` of
-// them are resident at once (LDS and wave slots); with fewer than two waves
-// per SIMD resident, the matrix pipes idle in proportion.
-double estimate(const Candidate& c, int64_t M, int64_t N) {
+// Estimated seconds of variant c on an M x N x K product.  Workgroups are
+// spread evenly over the CUs, so the busiest CU computes n = ceil(tiles /
+// CUs) tiles (charging partial-tile padding and the idle CUs of the last
+// round, i.e. wave quantisation), in rounds of up to occ resident ones.  In a
+// round of r tiles every slab takes the longer of its compute (r tiles'
+// flops at eff of the CU's peak, in proportion below kSaturate waves per
+// SIMD) and the latency of its loads; each round adds a fixed cost; and the
+// C tiles of the final round, which all CUs store at once, are charged at
+// the chip's write bandwidth.
+double estimate(const Candidate& c, int64_t M, int64_t N, int64_t K) {
   const Variant& v = c.v;
   const int64_t tiles = cdiv(M, v.tile_m) * cdiv(N, v.tile_n);
   const int64_t n = cdiv(tiles, kCUs);
-  const int waves = v.threads / 64;
-  int occ = kLdsPerCU / v.lds_bytes;
-  if (occ > kWavesPerCU / waves) occ = kWavesPerCU / waves;
-  if (occ < 1) occ = 1;
-  const double resident = (double)(n < occ ? n : occ);
-  const double per_simd = resident * waves / 4.0;
-  const double busy = per_simd >= kSaturate ? 1.0 : per_simd / kSaturate;
-  return (double)n * v.tile_m * v.tile_n / (c.tflops * busy);
+  const int64_t slabs = K > v.tile_k ? cdiv(K, v.tile_k) : 1;
+  const double waves = v.threads / 64.0;
+  const double slab_flops = 2.0 * v.tile_m * v.tile_n * v.tile_k;
+  auto round = [&](int64_t r) {
+    const double simd = r * waves / 4.0;
+    const double busy = simd >= kSaturate ? 1.0 : simd / kSaturate;
+    const double compute = r * slab_flops / (kPeakPerCU * c.eff * busy);
+    return (double)slabs * (compute > kSlabFloor ? compute : kSlabFloor) + kRoundCost;
+  };
+  const int64_t full = n / c.occ, rest = n % c.occ;
+  double t = (double)full * round(c.occ) + (rest > 0 ? round(rest) : 0.0);
+  const int64_t last = rest > 0 ? rest : c.occ;
+  const int64_t cus = tiles < kCUs ? tiles : kCUs;
+  t += (double)last * cus * v.tile_m * v.tile_n * 4.0 / kWriteBW;
+  return t;
 }
 
 // The candidate with the least estimated time; ties keep the earlier
 // (larger-tile) one.
-const Variant& choose_mfma(int64_t M, int64_t N, bool direct) {
+const Candidate& choose_mfma(int64_t M, int64_t N, int64_t K, bool direct) {
   int n;
   const Candidate* c = mfma_candidates(direct, n);
   int best = 0;
   double best_t = 0;
   for (int i = 0; i < n; ++i) {
-    const double t = estimate(c[i], M, N);
+    const double t = estimate(c[i], M, N, K);
     if (i == 0 || t < best_t * 0.995) {
       best = i;
       best_t = t;
     }
   }
-  return c[best].v;
+  return c[best];
 }
 
 KernelFn fma_fn(bool va, bool vb, bool vc) {
@@ -216,6 +238,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     p.info.threads = sg::kSimpleT * sg::kSimpleT;
     p.info.lds_bytes = 2 * sg::kSimpleT * sg::kSimpleT * 4;
     p.info.vec_a = p.info.vec_b = 0;
+    p.info.wg_per_cu = 8;  // 8 waves per SIMD at 44 registers per lane
     p.fn = sg::sgemm_simple_kernel;
     snprintf(p.info.kernel, sizeof(p.info.kernel), "simple_16x16x16");
   } else if (algo == SGEMM_ALGO_FMA) {
@@ -223,10 +246,13 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     p.info.tile_k = 16;
     p.info.threads = sg::FmaCfg::NT;
     p.info.lds_bytes = sg::FmaCfg::LDS_FLOATS * 4;
+    p.info.wg_per_cu = 4;  // 116 registers per lane: 4 waves per SIMD
     p.fn = fma_fn(va, vb, vc);
     set_name(p.info, "fma_128x128x16", va, vb);
   } else {
-    const Variant& v = choose_mfma(M, N, algo == SGEMM_ALGO_MFMA_DIRECT);
+    const Candidate& cand = choose_mfma(M, N, K, algo == SGEMM_ALGO_MFMA_DIRECT);
+    const Variant& v = cand.v;
+    p.info.wg_per_cu = cand.occ;
     p.info.tile_m = v.tile_m;
     p.info.tile_n = v.tile_n;
     p.info.tile_k = v.tile_k;
