@@ -19,7 +19,9 @@ is enqueued on.  Prints one JSON line.
 
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
 the counter scale factors) and prints its size.  ``--op transpose`` measures
-the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s).
+the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s,
+rotating over ``--buffers`` input/output pairs so that no launch is served
+from the last-level cache, with a plain copy of the same bytes beside it).
 """
 from __future__ import annotations
 
@@ -119,32 +121,42 @@ def bench_transpose(args) -> int:
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(7)
-    tin = torch.rand((rows, cols), device=dev, generator=g)
-    tout = torch.empty((cols, rows), device=dev)
+    # Launch i uses buffer pair i mod n: with n pairs spanning more than the
+    # 256 MiB last-level cache, every launch reads and writes HBM.
+    n = max(1, args.buffers)
+    tins = [torch.rand((rows, cols), device=dev, generator=g) for _ in range(n)]
+    touts = [torch.empty((cols, rows), device=dev) for _ in range(n)]
     stream = torch.cuda.current_stream(dev)
     code = sg.TRANSPOSE_LAYOUTS[args.layout]
 
-    def step():
-        st = sg.sgemm_transpose_ex(rows, cols, tin.data_ptr(), cols,
-                                   tout.data_ptr(), rows, stream.cuda_stream, code)
+    def step(i):
+        st = sg.sgemm_transpose_ex(rows, cols, tins[i % n].data_ptr(), cols,
+                                   touts[i % n].data_ptr(), rows,
+                                   stream.cuda_stream, code)
         if st != sg.OK:
             raise sg.SgemmError(st, "sgemm_transpose_ex")
 
-    for _ in range(args.warmup):
-        step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            fn(i)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+
+    wall, ev_ms = timed(step)
+    # Context: a device-to-device copy of the same bytes over the same buffers.
+    _, copy_ms = timed(lambda i: touts[i % n].view(-1).copy_(tins[i % n].view(-1)))
     nbytes = 2.0 * 4 * rows * cols
     achieved = nbytes / (float(ev_ms.mean()) / 1e3) / 1e9
+    copy_gbs = nbytes / (float(copy_ms.mean()) / 1e3) / 1e9
     print(json.dumps({
         "metric": "tiled transpose GB/s (fp32, 1 GPU)",
         "value": round(nbytes * args.steps / wall / 1e9, 1), "unit": "GB/s",
@@ -153,7 +165,9 @@ def bench_transpose(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"transpose {rows}x{cols} fp32, layout {args.layout}",
-                   "kernel_ms_median": round(float(np.median(ev_ms)), 5)},
+                   "buffer_pairs": n,
+                   "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+                   "copy_same_bytes_gbs": round(copy_gbs, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
@@ -178,6 +192,8 @@ def main() -> int:
     ap.add_argument("--op", default="sgemm", choices=["sgemm", "transpose"])
     ap.add_argument("--layout", default="auto",
                     choices=["auto", "naive", "padded", "swizzled"])
+    ap.add_argument("--buffers", type=int, default=4,
+                    help="transpose: buffer pairs the launches rotate over")
     ap.add_argument("--rows", type=int, default=8192)
     ap.add_argument("--cols", type=int, default=8192)
     args = ap.parse_args()

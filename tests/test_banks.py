@@ -122,9 +122,11 @@ def test_transpose_gather_naive_and_padded_conflict():
     # group; one extra unit per row leaves 4 distinct groups (4-way)
     for e in range(4):
         for w in range(4):
-            assert banks.conflict_degree(banks.transpose_gather("naive", e=e, wave=w),
-                                         banks.GFX950_BANKS) == 16
-            assert banks.conflict_degree(banks.transpose_gather("padded", e=e, wave=w),
-                                         banks.GFX950_BANKS) == 4
-            assert banks.conflict_degree(banks.transpose_gather("swizzled", e=e, wave=w),
-                                         banks.GFX950_BANKS) == 1
+            for bq in range(2):
+                kw = dict(e=e, wave=w, bq=bq)
+                assert banks.conflict_degree(banks.transpose_gather("naive", **kw),
+                                             banks.GFX950_BANKS) == 16
+                assert banks.conflict_degree(banks.transpose_gather("padded", **kw),
+                                             banks.GFX950_BANKS) == 4
+                assert banks.conflict_degree(banks.transpose_gather("swizzled", **kw),
+                                             banks.GFX950_BANKS) == 1

@@ -177,28 +177,30 @@ def fma_b_read(k: int = 0, half: int = 0) -> list[list[int]]:
 
 
 def transpose_unit(layout: str, r: int, c: int) -> int:
-    """16-byte unit of tile group (r, c) in the transpose kernel's layouts."""
+    """16-byte unit of tile group (r, c) in the transpose kernel's layouts
+    (tiles of 64 rows by 32 units)."""
     if layout == "padded":
-        return 17 * r + c
+        return 33 * r + c
     if layout == "swizzled":
-        return 16 * r + (c ^ ((r >> 2) & 15))
-    return 16 * r + c
+        return 32 * r + (c ^ (r >> 2))
+    return 32 * r + c
 
 
 def transpose_store(layout: str, q: int = 0, wave: int = 0) -> list[list[int]]:
-    """Tile row store (128-bit): thread f writes group (f / 16, f % 16)."""
+    """Tile row store (128-bit): thread f writes group (f / 32, f % 32)."""
     out = []
     for lane in range(64):
         f = q * 256 + 64 * wave + lane
-        out.append(vec(16 * transpose_unit(layout, f >> 4, f & 15), 16))
+        out.append(vec(16 * transpose_unit(layout, f >> 5, f & 31), 16))
     return out
 
 
-def transpose_gather(layout: str, e: int = 0, wave: int = 0) -> list[list[int]]:
+def transpose_gather(layout: str, e: int = 0, wave: int = 0,
+                     bq: int = 0) -> list[list[int]]:
     """Block read (128-bit): thread b reads group (4 (b % 16) + e, b / 16)."""
     out = []
     for lane in range(64):
-        b = 64 * wave + lane
+        b = 256 * bq + 64 * wave + lane
         out.append(vec(16 * transpose_unit(layout, 4 * (b & 15) + e, b >> 4), 16))
     return out
 
@@ -206,8 +208,10 @@ def transpose_gather(layout: str, e: int = 0, wave: int = 0) -> list[list[int]]:
 KERNEL_ACCESSES: dict[str, Callable[[], list[list[int]]]] = {
     "transpose padded store": lambda: transpose_store("padded", q=1, wave=2),
     "transpose swizzled store": lambda: transpose_store("swizzled", q=2, wave=3),
+    "transpose swizzled store, last round": lambda: transpose_store("swizzled", q=7, wave=3),
     "transpose swizzled gather": lambda: transpose_gather("swizzled", e=1, wave=2),
     "transpose swizzled gather, e = 3": lambda: transpose_gather("swizzled", e=3),
+    "transpose swizzled gather, second block": lambda: transpose_gather("swizzled", e=2, wave=1, bq=1),
     "transpose naive store": lambda: transpose_store("naive"),
     "direct A fragment read": direct_a_read,
     "direct A fragment read, k group 1, block 1": lambda: direct_a_read(i=1, e=1, sub=1),

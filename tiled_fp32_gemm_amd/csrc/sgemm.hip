@@ -348,8 +348,8 @@ int sgemm_transpose_ex(int64_t rows, int64_t cols, const float* in,
   a.cols = (int)cols;
   a.ldi = (int)(rows > 1 ? ldi : (cols > 1 ? cols : 1));
   a.ldo = (int)(cols > 1 ? ldo : (rows > 1 ? rows : 1));
-  a.tiles_x = (int)cdiv(cols, 64);
-  const int64_t tiles = cdiv(cols, 64) * cdiv(rows, 64);
+  a.tiles_x = (int)cdiv(cols, sg::kTransposeCols);
+  const int64_t tiles = cdiv(cols, sg::kTransposeCols) * cdiv(rows, sg::kTransposeRows);
   const bool vi = aligned16(in) && a.ldi % 4 == 0 && cols % 4 == 0;
   const bool vo = aligned16(out) && a.ldo % 4 == 0 && rows % 4 == 0;
   if (layout == SGEMM_TRANSPOSE_AUTO) layout = SGEMM_TRANSPOSE_SWIZZLED;
