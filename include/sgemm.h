@@ -146,8 +146,9 @@ int sgemm_plan_query(int64_t M, int64_t N, int64_t K,
  * out is cols x rows (row j at out + j*ldo, ldo >= max(1, rows)); out[j][i]
  * = in[i][j], bit for bit.  This is the pages' tiled transpose ("Memory-bank
  * mechanism and accelerated compute", section on the transpose kernel):
- * coalesced row reads and row writes, with the column access done inside a
- * 64 x 64 LDS tile.  Device pointers owned by the caller, 4-byte aligned, not
+ * coalesced row reads and row writes, with the column access done inside an
+ * LDS tile of 64 input rows by 128 input columns.  Device pointers owned by
+ * the caller, 4-byte aligned, not
  * overlapping; any leading dimension; enqueued on stream without
  * synchronising.  Errors as for sgemm (checked before any HIP call);
  * rows == 0 or cols == 0 is a no-op. */

@@ -26,7 +26,8 @@ def run_t(rows, cols, dIn: DevMat, dOut: DevMat, layout: str) -> None:
 
 
 SHAPES = [(1, 1), (1, 257), (257, 1), (63, 65), (64, 64), (65, 63), (100, 200),
-          (128, 4), (4, 128), (1000, 1500), (777, 4099), (2048, 64)]
+          (128, 4), (4, 128), (64, 128), (65, 129), (63, 127), (127, 255),
+          (1000, 1500), (777, 4099), (2048, 64)]
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
