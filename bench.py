@@ -17,6 +17,9 @@ is enqueued on.  Prints one JSON line.
   cpu_baseline     the CPU oracle on a bounded row sample of the same product,
                    repeated for about --cpu-seconds
 
+``--ladder`` runs every step of the ablation ladder (``sgemm_ladder``) on the
+workload instead, one JSON line per step.
+
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
 the counter scale factors) and prints its size.  ``--op transpose`` measures
 the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s,
@@ -175,6 +178,71 @@ def bench_transpose(args) -> int:
     return 0
 
 
+def bench_ladder(args) -> int:
+    """Every ablation ladder step (sgemm_ladder) on the workload: one JSON
+    line per step, in ladder order."""
+    import numpy as np
+    import torch
+
+    import seedgen
+    import tiled_fp32_gemm_amd as sg
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sg.load()
+    M, N, K, dist, seed = WORKLOADS[args.workload]
+    A, B = seedgen.gemm_inputs(M, N, K, dist, seed)
+    dev = torch.device("cuda:0")
+    tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    tC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ref = torch.empty_like(tC)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    if sg.sgemm(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N, ref.data_ptr(), N, sh) != sg.OK:
+        raise sg.SgemmError(sg.ERR_LAUNCH, "sgemm")
+    flops = 2.0 * M * N * K
+    for step, name in enumerate(sg.ladder_steps()):
+        def run():
+            st = sg.sgemm_ladder(step, M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
+                                 tC.data_ptr(), N, sh)
+            if st != sg.OK:
+                raise sg.SgemmError(st, "sgemm_ladder")
+        for _ in range(args.warmup):
+            run()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            run()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+        # every step computes the same product: compare with the product path
+        rel = float((tC - ref).abs().max() / ref.abs().max())
+        achieved = flops / (float(ev_ms.mean()) / 1e3) / 1e12
+        print(json.dumps({
+            "metric": "ablation ladder step TFLOP/s (fp32, 1 GPU)",
+            "value": round(flops * args.steps / wall / 1e12, 3), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall / args.steps * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"sgemm {args.workload}: M={M} N={N} K={K}",
+                       "ladder_step": step, "name": name,
+                       "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+                       "max_rel_diff_vs_sgemm": rel},
+            "roofline": {"bound": "mfma" if name.startswith("mfma") else "alu",
+                         "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                         "traffic": None},
+            "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -190,6 +258,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--op", default="sgemm", choices=["sgemm", "transpose"])
+    ap.add_argument("--ladder", action="store_true",
+                    help="run every ablation ladder step on the workload")
     ap.add_argument("--layout", default="auto",
                     choices=["auto", "naive", "padded", "swizzled"])
     ap.add_argument("--buffers", type=int, default=4,
@@ -215,6 +285,8 @@ def main() -> int:
         return 0
     if args.op == "transpose":
         return bench_transpose(args)
+    if args.ladder:
+        return bench_ladder(args)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)

@@ -186,6 +186,40 @@ const char *sgemm_status_string(int status);
 /* SGEMM_VERSION of the built library. */
 int sgemm_version(void);
 
+/* The ablation ladder: the pages' optimisations as separate kernels, each
+ * step changing one thing against the step before, for measurement
+ * ("CUDA in depth (4): accessing shared memory efficiently", sections on too
+ * many shared-memory reads, register tiling and going from 1x1 to 2x2;
+ * "CUDA in depth (5): vectorized load and shared-memory layout", sections on
+ * vector loads, the B-tile example and padding with transpose; "Memory-bank
+ * mechanism and accelerated compute", sections on one extra column and on
+ * alternatives to padding).  Every step computes C = A.B as sgemm does and
+ * takes the same arguments, checks and return codes; it is not the product
+ * path (call sgemm for that).
+ *   0  naive_global        one output per thread, no shared memory
+ *   1  lds_tile_16         16 x 16 tiles in LDS, one output per thread
+ *   2  reg_1x1             the same tiling, A stored k-major (transposed)
+ *   3  reg_2x2             2 x 2 outputs per thread (32 x 32 tile)
+ *   4  reg_4x4             4 x 4 (64 x 64 tile)
+ *   5  reg_8x8             8 x 8 (128 x 128 tile), 32-bit loads
+ *   6  reg_8x8_vec128      + 128-bit loads (32-bit where rows are unaligned)
+ *   7  .._a_unpadded      A without its 4-float padding (bank conflicts)
+ *   8  .._a_xor           A XOR-swizzled instead of padded
+ *   9  .._b_transposed    B stored transposed, Bs[BN][16] (bank conflicts)
+ *   10 .._b_transposed_padded  ... as Bs[BN][17]
+ *   11 reg_8x8_vec128_double_buffer  = sgemm_ex(..., SGEMM_ALGO_FMA)
+ *   12 mfma_register_staging         = sgemm_ex(..., SGEMM_ALGO_MFMA)
+ *   13 mfma_direct_to_lds            = sgemm_ex(..., SGEMM_ALGO_MFMA_DIRECT)
+ * sgemm_ladder_name returns NULL and sgemm_ladder SGEMM_ERR_INVALID_ARG for
+ * a step outside [0, sgemm_ladder_steps()). */
+int sgemm_ladder_steps(void);
+const char *sgemm_ladder_name(int step);
+int sgemm_ladder(int step, int64_t M, int64_t N, int64_t K,
+                 const float *A, int64_t lda,
+                 const float *B, int64_t ldb,
+                 float *C, int64_t ldc,
+                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,29 @@ def test_transpose_gather_naive_and_padded_conflict():
                                              banks.GFX950_BANKS) == 4
                 assert banks.conflict_degree(banks.transpose_gather("swizzled", **kw),
                                              banks.GFX950_BANKS) == 1
+
+
+def test_ladder_layouts_conflict_as_designed():
+    # the ladder's layout steps: A's split store 4-way without padding, free
+    # with it or with the XOR swizzle; B read down a column 16-way when
+    # transposed without padding, free with a 17-float pitch
+    for e in range(4):
+        for s in range(2):
+            for w in range(4):
+                kw = dict(e=e, s=s, wave=w)
+                assert banks.conflict_degree(banks.ladder_a_store("unpadded", **kw)) == 4
+                assert banks.conflict_degree(banks.ladder_a_store("padded", **kw)) == 1
+                assert banks.conflict_degree(banks.ladder_a_store("xor", **kw)) == 1
+    for k in range(16):
+        for col in range(4):
+            assert banks.conflict_degree(banks.ladder_b_read("cols", k=k, col=col)) == 16
+            assert banks.conflict_degree(banks.ladder_b_read("cols_padded", k=k, col=col)) == 1
+    # storing B transposed is a column walk too: a 16-float pitch puts a
+    # row's 32 groups in one bank, 17 floats leaves 2 groups per bank (lanes
+    # 16 groups apart, 16 * 4 * 17 floats = 68 * 16, a multiple of 64 apart)
+    for e in range(4):
+        for s in range(2):
+            for w in range(4):
+                kw = dict(e=e, s=s, wave=w)
+                assert banks.conflict_degree(banks.ladder_b_store("cols", **kw)) == 32
+                assert banks.conflict_degree(banks.ladder_b_store("cols_padded", **kw)) == 2

@@ -119,3 +119,17 @@ def test_direct_kernel_lds_traffic(asm, frag, ta, tb, subs):
     # LDS bytes per flop of the wave: 64 lanes x 4 B per word over 4096
     # flops per 32x32x2 instruction
     assert c["words"] * 4 * 64 / (c["mfma"] * 4096) == (ta + tb) / (16 * ta * tb)
+
+
+@pytest.mark.parametrize("tm,layout", [(1, "1ELi0"), (2, "1ELi0"), (4, "1ELi0"),
+                                       (8, "1ELi0"), (8, "1ELi1"), (8, "0ELi0")])
+def test_ladder_register_tiles_cut_lds_reads(asm, tm, layout):
+    """The ladder's TM x TM register tiles: LDS words read per multiply-add
+    equal (TM + TN) / (TM TN) -- 2, 1, 0.5 and 0.25 for 1x1 ... 8x8, in
+    whatever layout A and B take."""
+    body = kernel_body(asm, "sgemm_ladder_kernel", f"ILi{tm}ELi{tm}ELi{layout}ELb0E")
+    words = sum(READ_WORDS.get(i.split()[0], 0) for i in re.findall(
+        r"^\s+(ds_read\S*)", body, re.M))
+    fmas = len(re.findall(r"^\s+v_fmac?_f32(?:_e32|_e64)?\s", body, re.M))
+    assert fmas > 0
+    assert words / fmas == pytest.approx((tm + tm) / (tm * tm)), (words, fmas)

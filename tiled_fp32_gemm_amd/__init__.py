@@ -1,6 +1,7 @@
 """Python binding of the gfx950 SGEMM library (``include/sgemm.h``).
 
 The functions ``sgemm``, ``sgemm_ex``, ``sgemm_plan_query``,
+``sgemm_transpose``, ``sgemm_transpose_ex``, ``sgemm_ladder*``,
 ``sgemm_status_string`` and ``sgemm_version`` have the C names and arguments
 (device pointers as integers, a HIP stream handle as an integer) and only
 marshal arguments: every step of the product runs in the HIP kernels.
@@ -24,13 +25,16 @@ __all__ = ["sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_status_string",
            "sgemm_version", "matmul", "library_path", "load", "SgemmPlan",
            "SgemmError", "ALGOS", "OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED",
            "ERR_LAUNCH", "EXPORTED_SYMBOLS", "sgemm_transpose",
-           "sgemm_transpose_ex", "transpose", "TRANSPOSE_LAYOUTS"]
+           "sgemm_transpose_ex", "transpose", "TRANSPOSE_LAYOUTS",
+           "sgemm_ladder", "sgemm_ladder_steps", "sgemm_ladder_name",
+           "ladder_steps"]
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
 ALGOS = {"auto": 0, "simple": 1, "fma": 2, "mfma": 3, "mfma_direct": 4}
 EXPORTED_SYMBOLS = ("sgemm", "sgemm_ex", "sgemm_plan_query",
                     "sgemm_transpose", "sgemm_transpose_ex",
-                    "sgemm_status_string", "sgemm_version")
+                    "sgemm_status_string", "sgemm_version",
+                    "sgemm_ladder_steps", "sgemm_ladder_name", "sgemm_ladder")
 TRANSPOSE_LAYOUTS = {"auto": 0, "naive": 1, "padded": 2, "swizzled": 3}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +95,12 @@ def load():
     lib.sgemm_status_string.restype = ctypes.c_char_p
     lib.sgemm_version.argtypes = []
     lib.sgemm_version.restype = i32
+    lib.sgemm_ladder_steps.argtypes = []
+    lib.sgemm_ladder_steps.restype = i32
+    lib.sgemm_ladder_name.argtypes = [i32]
+    lib.sgemm_ladder_name.restype = ctypes.c_char_p
+    lib.sgemm_ladder.argtypes = [i32] + common + [fp]
+    lib.sgemm_ladder.restype = i32
     _lib = lib
     return lib
 
@@ -141,6 +151,25 @@ def transpose(A, out=None, layout: str | int = "auto", stream=None):
     if st != OK:
         raise SgemmError(st, "sgemm_transpose_ex")
     return out
+
+
+def sgemm_ladder_steps() -> int:
+    return load().sgemm_ladder_steps()
+
+
+def sgemm_ladder_name(step: int) -> str | None:
+    name = load().sgemm_ladder_name(step)
+    return None if name is None else name.decode()
+
+
+def sgemm_ladder(step, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """Ablation ladder step ``step`` of C = A·B; returns the status code."""
+    return load().sgemm_ladder(step, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def ladder_steps() -> list[str]:
+    """Names of the ablation ladder's steps, in order."""
+    return [sgemm_ladder_name(i) for i in range(sgemm_ladder_steps())]
 
 
 def sgemm_status_string(status: int) -> str:

@@ -205,6 +205,44 @@ def transpose_gather(layout: str, e: int = 0, wave: int = 0,
     return out
 
 
+def ladder_a_store(layout: str, e: int = 0, s: int = 0,
+                   wave: int = 0) -> list[list[int]]:
+    """Ladder 8x8 kernel: A's k-major split store (32-bit), element e of the
+    groups of slot s.  layout: "unpadded" As[16][128], "padded" As[16][132],
+    "xor" As[16][128] with the row XORed by 16 ((k / 4) mod 4)."""
+    ra = 132 if layout == "padded" else 128
+    out = []
+    for lane in range(64):
+        f = s * 256 + 64 * wave + lane
+        row, kq = (f & 15) + ((f >> 6) << 4), (f >> 4) & 3
+        k = 4 * kq + e
+        col = row ^ (16 * ((k >> 2) & 3)) if layout == "xor" else row
+        out.append([4 * (k * ra + col)])
+    return out
+
+
+def ladder_b_store(layout: str, e: int = 0, s: int = 0,
+                   wave: int = 0) -> list[list[int]]:
+    """Ladder 8x8 kernel with B transposed: element e of group (k, jq) =
+    (f / 32, f % 32) goes to Bs[4 jq + e][k] (32-bit): "cols" pitch 16,
+    "cols_padded" pitch 17."""
+    rb = 17 if layout == "cols_padded" else 16
+    out = []
+    for lane in range(64):
+        f = s * 256 + 64 * wave + lane
+        k, jq = f // 32, f % 32
+        out.append([4 * ((4 * jq + e) * rb + k)])
+    return out
+
+
+def ladder_b_read(layout: str, k: int = 0, col: int = 0,
+                  wave: int = 0) -> list[list[int]]:
+    """Ladder 8x8 kernel with B transposed (32-bit read of column 4 tx + col
+    at depth k): "cols" Bs[128][16], "cols_padded" Bs[128][17]."""
+    rb = 17 if layout == "cols_padded" else 16
+    return [[4 * ((4 * (lane & 15) + col) * rb + k)] for lane in range(64)]
+
+
 KERNEL_ACCESSES: dict[str, Callable[[], list[list[int]]]] = {
     "transpose padded store": lambda: transpose_store("padded", q=1, wave=2),
     "transpose swizzled store": lambda: transpose_store("swizzled", q=2, wave=3),
@@ -226,6 +264,9 @@ KERNEL_ACCESSES: dict[str, Callable[[], list[list[int]]]] = {
     "register B store": reg_b_store,
     "register B read": reg_b_read,
     "register B read, 64 columns": lambda: reg_b_read(bn=64, p=3),
+    "ladder A store, padded": lambda: ladder_a_store("padded", e=1, s=1, wave=2),
+    "ladder A store, XOR": lambda: ladder_a_store("xor", e=3, s=0, wave=1),
+    "ladder B transposed read, padded": lambda: ladder_b_read("cols_padded", k=5, col=2),
     "FMA A transposed store": fma_a_store,
     "FMA A transposed store, element 3": lambda: fma_a_store(e=3, f0=192),
     "FMA A read": fma_a_read,

@@ -7,6 +7,7 @@
 
 #include "../../include/sgemm.h"
 #include "kernel_fma.hpp"
+#include "kernel_ladder.hpp"
 #include "kernel_mfma.hpp"
 #include "kernel_mfma_direct.hpp"
 #include "kernel_simple.hpp"
@@ -267,19 +268,12 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-int sgemm_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-             const float* B, int64_t ldb, float* C, int64_t ldc,
-             hipStream_t stream, int algo) {
-  Checked c;
-  const int st = check(M, N, K, A, lda, B, ldb, C, ldc, algo, c);
-  if (st != SGEMM_OK || !c.launch) return st;
-  const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, algo);
-  if (p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;  // no kernel for this form
-
+// Kernel arguments for checked operands and a launch of fn over the tiles
+// of C.
+int launch_gemm(KernelFn fn, int64_t M, int64_t N, int64_t K, const float* A,
+                int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                const Checked& c, int tile_m, int tile_n, int threads,
+                hipStream_t stream) {
   GemmArgs g;
   g.A = A;
   g.B = B;
@@ -294,16 +288,99 @@ int sgemm_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   g.lda = (int)(M > 1 ? lda : (K > 1 ? K : 1));
   g.ldb = (int)(K > 1 ? ldb : (N > 1 ? N : 1));
   g.ldc = (int)(M > 1 ? ldc : (N > 1 ? N : 1));
-  g.tiles_m = (int)cdiv(M, p.info.tile_m);
-  g.tiles_n = (int)cdiv(N, p.info.tile_n);
+  g.tiles_m = (int)cdiv(M, tile_m);
+  g.tiles_n = (int)cdiv(N, tile_n);
   g.group_m = g.tiles_m < 8 ? g.tiles_m : 8;
 
   void* kargs[] = {&g};
-  const hipError_t e =
-      hipLaunchKernel(reinterpret_cast<const void*>(p.fn),
-                      dim3((unsigned)p.info.workgroups), dim3(p.info.threads),
-                      kargs, 0, stream);
+  const hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(fn),
+      dim3((unsigned)((int64_t)g.tiles_m * g.tiles_n)), dim3(threads), kargs, 0, stream);
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+// The ablation ladder.  Each step changes one thing against the one before;
+// the vector-ALU steps 0-10 run the kernels of kernel_ladder.hpp (and the
+// pages' basic tiled loop, kernel_simple.hpp), the last three the product
+// families.  Steps with 128-bit loads fall back to 32-bit ones when A or B
+// rows are not 16-byte aligned.
+struct LadderStep {
+  const char* name;
+  KernelFn vec, sca;  // 128-bit / 32-bit load forms (same for the others)
+  int tile_m, tile_n;
+  int algo;           // >= 0: the step is the product family sgemm_ex(algo)
+};
+
+template <int TM, int TN, int AL, int BL, bool VEC>
+LadderStep ladder_step(const char* name) {
+  return {name, sg::sgemm_ladder_kernel<TM, TN, AL, BL, VEC>,
+          sg::sgemm_ladder_kernel<TM, TN, AL, BL, false>, 16 * TM, 16 * TN, -1};
+}
+
+const LadderStep* ladder_steps(int& n) {
+  static const LadderStep steps[] = {
+      {"naive_global", sg::sgemm_naive_kernel, sg::sgemm_naive_kernel, 16, 16, -1},
+      {"lds_tile_16", sg::sgemm_simple_kernel, sg::sgemm_simple_kernel, 16, 16, -1},
+      ladder_step<1, 1, sg::kAPadded, sg::kBRows, false>("reg_1x1"),
+      ladder_step<2, 2, sg::kAPadded, sg::kBRows, false>("reg_2x2"),
+      ladder_step<4, 4, sg::kAPadded, sg::kBRows, false>("reg_4x4"),
+      ladder_step<8, 8, sg::kAPadded, sg::kBRows, false>("reg_8x8"),
+      ladder_step<8, 8, sg::kAPadded, sg::kBRows, true>("reg_8x8_vec128"),
+      ladder_step<8, 8, sg::kAUnpadded, sg::kBRows, true>("reg_8x8_vec128_a_unpadded"),
+      ladder_step<8, 8, sg::kASwizzled, sg::kBRows, true>("reg_8x8_vec128_a_xor"),
+      ladder_step<8, 8, sg::kAPadded, sg::kBCols, true>("reg_8x8_vec128_b_transposed"),
+      ladder_step<8, 8, sg::kAPadded, sg::kBColsPadded, true>(
+          "reg_8x8_vec128_b_transposed_padded"),
+      {"reg_8x8_vec128_double_buffer", nullptr, nullptr, 0, 0, SGEMM_ALGO_FMA},
+      {"mfma_register_staging", nullptr, nullptr, 0, 0, SGEMM_ALGO_MFMA},
+      {"mfma_direct_to_lds", nullptr, nullptr, 0, 0, SGEMM_ALGO_MFMA_DIRECT}};
+  n = (int)(sizeof(steps) / sizeof(steps[0]));
+  return steps;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+             const float* B, int64_t ldb, float* C, int64_t ldc,
+             hipStream_t stream, int algo) {
+  Checked c;
+  const int st = check(M, N, K, A, lda, B, ldb, C, ldc, algo, c);
+  if (st != SGEMM_OK || !c.launch) return st;
+  const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, algo);
+  if (p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;  // no kernel for this form
+
+  return launch_gemm(p.fn, M, N, K, A, lda, B, ldb, C, ldc, c, p.info.tile_m,
+                     p.info.tile_n, p.info.threads, stream);
+}
+
+int sgemm_ladder_steps(void) {
+  int n;
+  ladder_steps(n);
+  return n;
+}
+
+const char* sgemm_ladder_name(int step) {
+  int n;
+  const LadderStep* s = ladder_steps(n);
+  return (step >= 0 && step < n) ? s[step].name : nullptr;
+}
+
+int sgemm_ladder(int step, int64_t M, int64_t N, int64_t K, const float* A,
+                 int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                 hipStream_t stream) {
+  int n;
+  const LadderStep* steps = ladder_steps(n);
+  if (step < 0 || step >= n) return SGEMM_ERR_INVALID_ARG;
+  const LadderStep& ls = steps[step];
+  if (ls.algo >= 0) return sgemm_ex(M, N, K, A, lda, B, ldb, C, ldc, stream, ls.algo);
+  Checked c;
+  const int st = check(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_AUTO, c);
+  if (st != SGEMM_OK || !c.launch) return st;
+  const bool vec = K == 0 || (vec_a_ok(A, lda, K) && vec_b_ok(B, ldb, N));
+  return launch_gemm(vec ? ls.vec : ls.sca, M, N, K, A, lda, B, ldb, C, ldc, c,
+                     ls.tile_m, ls.tile_n, 256, stream);
 }
 
 int sgemm(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
