@@ -54,14 +54,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.txt")
 
 
 def kernel_source_hash() -> str:
-    """Digest of the sources of the GEMM kernels (device code only): the
-    counters recorded under profiles/ stay valid while it is unchanged."""
+    """Digest of the sources of the product GEMM kernels (device code only;
+    not the transpose, not the ablation ladder's own kernels): the counters
+    recorded under profiles/ stay valid while it is unchanged."""
     from tiled_fp32_gemm_amd import build
     h = hashlib.sha256()
     for p in build.sources():
         name = os.path.basename(p)
         if name == "common.hpp" or (name.startswith("kernel_")
-                                    and "transpose" not in name):
+                                    and "transpose" not in name
+                                    and "ladder" not in name):
             h.update(name.encode())
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
