@@ -168,3 +168,27 @@ def test_transpose_checks(lib, args, status):
     ldo = args.get("ldo", max(rows, 1))
     assert sg.sgemm_transpose_ex(rows, cols, inp, ldi, out, ldo, 0,
                                  args.get("layout", 0)) == status
+
+
+def test_ladder_steps_and_names(lib):
+    names = sg.ladder_steps()
+    assert len(names) == sg.sgemm_ladder_steps() == 14
+    assert names[0] == "naive_global" and names[-1] == "mfma_direct_to_lds"
+    assert sg.sgemm_ladder_name(-1) is None and sg.sgemm_ladder_name(14) is None
+
+
+@pytest.mark.parametrize("step", [0, 5, 9, 11, 13])
+def test_ladder_checks_before_any_hip_call(lib, step):
+    # the same checks as sgemm, all answered on the host
+    B, C = BIG + (1 << 31), BIG + (1 << 32)
+    assert sg.sgemm_ladder(step, -1, 4, 4, BIG, 4, B, 4, C, 4) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_ladder(step, 4, 4, 8, BIG, 7, B, 4, C, 4) == sg.ERR_INVALID_ARG   # lda < K
+    assert sg.sgemm_ladder(step, 4, 4, 4, BIG, 4, B, 4, BIG + 8, 4) == sg.ERR_INVALID_ARG  # overlap
+    assert sg.sgemm_ladder(step, 4, 4, 4, 0, 4, B, 4, C, 4) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_ladder(step, 0, 5, 5, 0, 5, 0, 5, 0, 5) == sg.OK   # nothing to do
+
+
+def test_ladder_rejects_unknown_steps(lib):
+    B, C = BIG + (1 << 31), BIG + (1 << 32)
+    for step in (-1, 14, 1 << 20):
+        assert sg.sgemm_ladder(step, 4, 4, 4, BIG, 4, B, 4, C, 4) == sg.ERR_INVALID_ARG
