@@ -271,8 +271,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs "
-              "the kernel on one GPU only (one GPU's share of a sharded "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark "
+              "runs the kernel on one GPU (one GPU's share of a sharded "
               "product is the same kernel at a smaller shape)", file=sys.stderr)
         return 2
 
