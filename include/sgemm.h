@@ -69,7 +69,7 @@ typedef struct ihipStream_t *hipStream_t;
 extern "C" {
 #endif
 
-#define SGEMM_VERSION 110 /* 1.1.0 */
+#define SGEMM_VERSION 120 /* 1.2.0 */
 
 /* Status codes. */
 #define SGEMM_OK 0
@@ -133,6 +133,9 @@ typedef struct sgemm_plan {
     int lds_bytes;       /* LDS per workgroup */
     int wg_per_cu;       /* workgroups one CU holds at once (LDS and
                             registers of the kernel as built for gfx950) */
+    int splits;          /* K ranges run by separate workgroups: 1, or > 1
+                            for a split plan (sgemm_plan_query_ws) */
+    int64_t workspace_bytes; /* workspace the plan uses (0 unless split) */
     char kernel[64];     /* kernel name, NUL-terminated */
 } sgemm_plan;
 
@@ -141,6 +144,49 @@ int sgemm_plan_query(int64_t M, int64_t N, int64_t K,
                      const float *B, int64_t ldb,
                      const float *C, int64_t ldc,
                      int algo, sgemm_plan *plan);
+
+/* C = A·B with K split across workgroups when that is faster: for a C too
+ * small to fill the 256 CUs with its tiles but a long K, S workgroups per C
+ * tile each multiply one range of K (the per-tile product of "CUDA in depth
+ * (4): accessing shared memory efficiently", section on too many
+ * shared-memory reads, over a part of the k sum) into partial tiles in
+ * workspace, and a second kernel adds the S partials in the order s = 0..S-1
+ * into C.  The result is deterministic from run to run and within the sgemm
+ * tolerance, but is not bitwise equal to sgemm() for such shapes (the k sum
+ * is grouped differently).  Without a split (the shape fills the chip, or
+ * workspace_bytes is below what the best split needs) this is exactly
+ * sgemm(), bit for bit, and the workspace is not touched.
+ *   workspace        device memory owned by the caller, 4-byte aligned, not
+ *                    overlapping A, B or C; its contents on entry do not
+ *                    matter and are overwritten (S x M x N floats).  It must
+ *                    stay allocated until the enqueued kernels finish, and
+ *                    calls that share one workspace must be ordered (one
+ *                    stream), or they race.  May be NULL when
+ *                    workspace_bytes is 0.
+ *   workspace_bytes  its size; 0 allows no split.
+ * Other arguments, checks and return codes are sgemm's; a negative size, a
+ * NULL workspace of nonzero size, a misaligned or overlapping workspace is
+ * SGEMM_ERR_INVALID_ARG.  No allocation; two kernel launches on stream. */
+int sgemm_ws(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             hipStream_t stream, void *workspace, int64_t workspace_bytes);
+
+/* The workspace size with which sgemm_ws takes its fastest plan for
+ * M x N x K (0 when the best plan does not split K, or for an invalid or
+ * empty shape).  Host only; no HIP call. */
+int64_t sgemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* The plan sgemm_ws would take with this workspace size (plan->splits and
+ * plan->workspace_bytes give the split).  Checks as for sgemm_plan_query
+ * with AUTO; a negative workspace_bytes or NULL plan is
+ * SGEMM_ERR_INVALID_ARG. */
+int sgemm_plan_query_ws(int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda,
+                        const float *B, int64_t ldb,
+                        const float *C, int64_t ldc,
+                        int64_t workspace_bytes, sgemm_plan *plan);
 
 /* out = in^T: in is rows x cols (row i at in + i*ldi, ldi >= max(1, cols)),
  * out is cols x rows (row j at out + j*ldo, ldo >= max(1, rows)); out[j][i]

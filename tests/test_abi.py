@@ -44,7 +44,7 @@ def test_one_hip_runtime_is_mapped(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert sg.sgemm_version() == 110
+    assert sg.sgemm_version() == 120
     assert sg.sgemm_status_string(sg.OK) == "success"
     for st in (sg.ERR_INVALID_ARG, sg.ERR_UNSUPPORTED, sg.ERR_LAUNCH):
         assert sg.sgemm_status_string(st) not in ("", "success")
@@ -192,3 +192,78 @@ def test_ladder_rejects_unknown_steps(lib):
     B, C = BIG + (1 << 31), BIG + (1 << 32)
     for step in (-1, 14, 1 << 20):
         assert sg.sgemm_ladder(step, 4, 4, 4, BIG, 4, B, 4, C, 4) == sg.ERR_INVALID_ARG
+
+
+# Split K across workgroups (sgemm_ws): plans, sizes and argument checks.
+WS = BIG + (3 << 31)   # a fake workspace address past A, B and C
+
+
+def call_ws(M, N, K, ws_bytes, lda=None, ldb=None, ldc=None):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return sg.sgemm_plan_query_ws(M, N, K, BIG, lda, BIG + (1 << 31), ldb,
+                                  BIG + (1 << 32), ldc, ws_bytes)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (256, 256, 8192),
+                                   (1000, 1500, 777), (64, 64, 65536),
+                                   (100, 70, 0), (0, 8, 8)])
+def test_ws_plan_without_workspace_is_the_plain_plan(lib, M, N, K):
+    st0, p0 = call(M, N, K)
+    st1, p1 = call_ws(M, N, K, 0)
+    assert st0 == st1 == sg.OK
+    assert p1.as_dict() == p0.as_dict()
+    assert p1.splits == 1 and p1.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 8192), (64, 64, 65536),
+                                   (32, 4096, 4096), (200, 300, 10001),
+                                   (768, 768, 12288), (1, 1024, 65536),
+                                   (1024, 1, 32768)])
+def test_split_plans_for_underfilled_long_k(lib, M, N, K):
+    need = sg.sgemm_workspace_bytes(M, N, K)
+    st, p = call_ws(M, N, K, need)
+    assert st == sg.OK and need > 0
+    assert p.splits > 1 and p.workspace_bytes == need == p.splits * M * N * 4
+    assert p.kernel.decode().endswith(f"_split{p.splits}")
+    assert p.workgroups == -(-M // p.tile_m) * -(-N // p.tile_n) * p.splits
+    # a larger workspace gives the same plan; a smaller one a smaller split
+    # that fits it, or none
+    assert call_ws(M, N, K, 1 << 30)[1].as_dict() == p.as_dict()
+    st2, p2 = call_ws(M, N, K, need - 4)
+    assert st2 == sg.OK and p2.workspace_bytes <= need - 4
+    assert p2.splits < p.splits or p2.as_dict() != p.as_dict()
+    st3, p3 = call_ws(M, N, K, 2 * M * N * 4 - 4)   # not even two partials
+    assert st3 == sg.OK and p3.splits == 1 and p3.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (8192, 8192, 8192),
+                                   (65536, 128, 256), (256, 256, 256),
+                                   (2048, 2048, 2048), (100, 100, 0)])
+def test_no_split_where_the_chip_is_filled(lib, M, N, K):
+    assert sg.sgemm_workspace_bytes(M, N, K) == 0
+    st, p = call_ws(M, N, K, 1 << 30)
+    assert st == sg.OK and p.splits == 1 and p.as_dict() == call(M, N, K)[1].as_dict()
+
+
+def test_workspace_bytes_of_invalid_or_empty_shapes(lib):
+    for M, N, K in ((-1, 4, 4), (4, -1, 4), (4, 4, -1), (0, 4, 4096), (4, 0, 4096)):
+        assert sg.sgemm_workspace_bytes(M, N, K) == 0
+
+
+def test_ws_argument_checks_before_any_hip_call(lib):
+    M, N, K = 256, 256, 8192
+    need = sg.sgemm_workspace_bytes(M, N, K)
+    A, B, C = BIG, BIG + (1 << 31), BIG + (1 << 32)
+    bad = [(WS, -4), (0, need), (WS + 2, need),      # negative, null, misaligned
+           (A + 64, need), (B, need), (C - 16, need)]  # overlaps A, B, C
+    for ws, nb in bad:
+        assert sg.sgemm_ws(M, N, K, A, K, B, N, C, N, 0, ws, nb) == sg.ERR_INVALID_ARG, (ws, nb)
+    # the sgemm checks come first, and apply with a workspace as well
+    assert sg.sgemm_ws(M, N, K, A, K - 1, B, N, C, N, 0, WS, need) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_ws(M, N, K, 0, K, B, N, C, N, 0, WS, need) == sg.ERR_INVALID_ARG
+    assert sg.sgemm_ws(0, N, K, 0, K, 0, N, 0, N, 0, 0, 0) == sg.OK   # empty: no-op
+    st, _ = sg.sgemm_plan_query_ws(M, N, K, A, K, B, N, C, N, -1)
+    assert st == sg.ERR_INVALID_ARG
+    assert lib.sgemm_plan_query_ws(M, N, K, A, K, B, N, C, N, need, None) == sg.ERR_INVALID_ARG

@@ -1,4 +1,5 @@
-"""The library's launches under HIP graph capture: sgemm and sgemm_transpose
+"""The library's launches under HIP graph capture: sgemm, sgemm_ws (K split
+across workgroups, two kernels through a workspace) and sgemm_transpose
 enqueue only kernel launches (no memsets, no allocation, no synchronisation),
 so a captured sequence replays to the same bits as the eager calls.  The
 graph is replayed several times with eager work and synchronisation between
@@ -26,6 +27,15 @@ def test_captured_products_replay_bit_exact():
         A, B = seedgen.gemm_inputs(M, N, K, "normal", 1300 + idx)
         ops.append((M, N, K, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
                     torch.empty((M, N), device=dev)))
+    # split products: (M, N, K, A, B, C), one workspace shared in stream order
+    splits = []
+    for idx, (M, N, K) in enumerate([(256, 256, 8192), (200, 300, 10001)]):
+        A, B = seedgen.gemm_inputs(M, N, K, "normal", 1350 + idx)
+        assert sg.sgemm_workspace_bytes(M, N, K) > 0
+        splits.append((M, N, K, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev),
+                       torch.empty((M, N), device=dev)))
+    ws_bytes = max(sg.sgemm_workspace_bytes(M, N, K) for M, N, K, *_ in splits)
+    ws = torch.empty(ws_bytes // 4, device=dev)
     tin = torch.rand((1000, 1500), device=dev)
     tout = torch.empty((1500, 1000), device=dev)
 
@@ -34,13 +44,17 @@ def test_captured_products_replay_bit_exact():
         for M, N, K, tA, tB, tC in ops:
             assert sg.sgemm(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
                             tC.data_ptr(), N, s) == sg.OK
+        for M, N, K, tA, tB, tC in splits:
+            assert sg.sgemm_ws(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
+                               tC.data_ptr(), N, s, ws.data_ptr(), ws_bytes) == sg.OK
         assert sg.sgemm_transpose(1000, 1500, tin.data_ptr(), 1500,
                                   tout.data_ptr(), 1000, s) == sg.OK
 
     say("[gpu] graph: eager reference")
     enqueue()
     torch.cuda.synchronize()
-    want = [op[5].clone() for op in ops] + [tout.clone()]
+    outs = ops + splits
+    want = [op[5].clone() for op in outs] + [tout.clone()]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -54,14 +68,15 @@ def test_captured_products_replay_bit_exact():
     with torch.cuda.graph(graph):
         enqueue()
     for rep in range(4):
-        for op in ops:
+        for op in outs:
             op[5].fill_(float("nan"))
+        ws.fill_(float("nan"))
         tout.fill_(float("nan"))
         torch.cuda.synchronize()
         say(f"[gpu] graph: replay {rep}")
         graph.replay()
         torch.cuda.synchronize()
-        got = [op[5] for op in ops] + [tout]
+        got = [op[5] for op in outs] + [tout]
         for w, g in zip(want, got):
             assert torch.equal(w, g), rep
         # eager work of the program between the replays

@@ -1,6 +1,7 @@
 """Python binding of the gfx950 SGEMM library (``include/sgemm.h``).
 
-The functions ``sgemm``, ``sgemm_ex``, ``sgemm_plan_query``,
+The functions ``sgemm``, ``sgemm_ex``, ``sgemm_ws``,
+``sgemm_workspace_bytes``, ``sgemm_plan_query``, ``sgemm_plan_query_ws``,
 ``sgemm_transpose``, ``sgemm_transpose_ex``, ``sgemm_ladder*``,
 ``sgemm_status_string`` and ``sgemm_version`` have the C names and arguments
 (device pointers as integers, a HIP stream handle as an integer) and only
@@ -27,14 +28,16 @@ __all__ = ["sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_status_string",
            "ERR_LAUNCH", "EXPORTED_SYMBOLS", "sgemm_transpose",
            "sgemm_transpose_ex", "transpose", "TRANSPOSE_LAYOUTS",
            "sgemm_ladder", "sgemm_ladder_steps", "sgemm_ladder_name",
-           "ladder_steps"]
+           "ladder_steps", "sgemm_ws", "sgemm_workspace_bytes",
+           "sgemm_plan_query_ws"]
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
 ALGOS = {"auto": 0, "simple": 1, "fma": 2, "mfma": 3, "mfma_direct": 4}
 EXPORTED_SYMBOLS = ("sgemm", "sgemm_ex", "sgemm_plan_query",
                     "sgemm_transpose", "sgemm_transpose_ex",
                     "sgemm_status_string", "sgemm_version",
-                    "sgemm_ladder_steps", "sgemm_ladder_name", "sgemm_ladder")
+                    "sgemm_ladder_steps", "sgemm_ladder_name", "sgemm_ladder",
+                    "sgemm_ws", "sgemm_workspace_bytes", "sgemm_plan_query_ws")
 TRANSPOSE_LAYOUTS = {"auto": 0, "naive": 1, "padded": 2, "swizzled": 3}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +58,7 @@ class SgemmPlan(ctypes.Structure):
                 ("threads", ctypes.c_int), ("vec_a", ctypes.c_int),
                 ("vec_b", ctypes.c_int), ("workgroups", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int), ("wg_per_cu", ctypes.c_int),
+                ("splits", ctypes.c_int), ("workspace_bytes", ctypes.c_int64),
                 ("kernel", ctypes.c_char * 64)]
 
     def as_dict(self) -> dict:
@@ -101,6 +105,12 @@ def load():
     lib.sgemm_ladder_name.restype = ctypes.c_char_p
     lib.sgemm_ladder.argtypes = [i32] + common + [fp]
     lib.sgemm_ladder.restype = i32
+    lib.sgemm_ws.argtypes = common + [fp, fp, i64]
+    lib.sgemm_ws.restype = i32
+    lib.sgemm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.sgemm_workspace_bytes.restype = i64
+    lib.sgemm_plan_query_ws.argtypes = common + [i64, ctypes.POINTER(SgemmPlan)]
+    lib.sgemm_plan_query_ws.restype = i32
     _lib = lib
     return lib
 
@@ -120,6 +130,26 @@ def sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, algo=0):
     plan = SgemmPlan()
     st = load().sgemm_plan_query(M, N, K, A, lda, B, ldb, C, ldc, algo,
                                  ctypes.byref(plan))
+    return st, plan
+
+
+def sgemm_ws(M, N, K, A, lda, B, ldb, C, ldc, stream=0, workspace=0,
+             workspace_bytes=0) -> int:
+    """``sgemm`` that may split K across workgroups into ``workspace``."""
+    return load().sgemm_ws(M, N, K, A, lda, B, ldb, C, ldc, stream, workspace,
+                           workspace_bytes)
+
+
+def sgemm_workspace_bytes(M, N, K) -> int:
+    """Workspace bytes for ``sgemm_ws``'s fastest plan (0: no split)."""
+    return load().sgemm_workspace_bytes(M, N, K)
+
+
+def sgemm_plan_query_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace_bytes=0):
+    """``(status, SgemmPlan)`` for what ``sgemm_ws`` would launch."""
+    plan = SgemmPlan()
+    st = load().sgemm_plan_query_ws(M, N, K, A, lda, B, ldb, C, ldc,
+                                    workspace_bytes, ctypes.byref(plan))
     return st, plan
 
 

@@ -71,6 +71,11 @@ struct GemmArgs {
   int lda, ldb, ldc;
   int tiles_m, tiles_n;                // C tiles along M and N
   int group_m;                         // tile rows per ordering group
+  // Split K across workgroups (kernels instantiated for it only): split s
+  // covers k in [s k_split, min((s + 1) k_split, K)) and writes its partial
+  // tile to W + s M N (rows of N floats).
+  int splits, k_split;
+  float* W;
 };
 
 // Workgroup -> C tile.  Workgroups are handed to the 8 XCDs round-robin
@@ -85,6 +90,28 @@ __device__ __forceinline__ void tile_of_workgroup(const GemmArgs& g, int& tm,
   const int q = nwg >> 3, rem = nwg & 7;
   const int xcd = w & 7, local = w >> 3;
   const int L = xcd * q + (xcd < rem ? xcd : rem) + local;
+  const int per_group = g.group_m * g.tiles_n;
+  const int grp = L / per_group;
+  const int first_m = grp * g.group_m;
+  const int rows = min(g.tiles_m - first_m, g.group_m);
+  const int in_grp = L - grp * per_group;
+  tm = first_m + in_grp % rows;
+  tn = in_grp / rows;
+}
+
+// Workgroup -> (split, C tile) for a grid of splits x tiles workgroups: the
+// same XCD renumbering over the whole grid, split-major, so that an XCD holds
+// neighbouring tiles of one K range at a time.
+__device__ __forceinline__ void tile_split_of_workgroup(const GemmArgs& g, int& tm,
+                                                        int& tn, int& split) {
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int nwg = tiles * g.splits;
+  const int w = (int)blockIdx.x;
+  const int q = nwg >> 3, rem = nwg & 7;
+  const int xcd = w & 7, local = w >> 3;
+  int L = xcd * q + (xcd < rem ? xcd : rem) + local;
+  split = L / tiles;
+  L -= split * tiles;
   const int per_group = g.group_m * g.tiles_n;
   const int grp = L / per_group;
   const int first_m = grp * g.group_m;

@@ -54,6 +54,11 @@
 // Split K inside the workgroup (KS > 1, for shapes with too few tiles to fill
 // the chip): KS wave groups compute the same tile over their own sub-slabs
 // of every slab; the partial tiles are summed through LDS in group order.
+//
+// Split K across workgroups (SPLIT, for grids that even the smallest tiles
+// leave under-filled): workgroup (s, tile) computes the tile over the s-th
+// range of k_split values of K into a partial buffer; sgemm_split_reduce
+// (kernel_reduce.hpp) then adds the partials in split order.
 #pragma once
 
 #include "common.hpp"
@@ -115,9 +120,9 @@ __device__ __forceinline__ void wait_slabs(int ahead) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3,
-          int KS_ = 1>
+          int KS_ = 1, bool SPLIT = false>
 __global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN) * KS_)
-sgemm_mfma_direct_kernel(GemmArgs g) {
+sgemm_mfma_direct_kernel(GemmArgs g_in) {
   using Cfg = DirectCfg<BM, BN, WM, WN, BK_, STAGES_, KS_>;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
   constexpr int CPR = Cfg::CPR, STAGES = Cfg::STAGES, DEPTH = Cfg::DEPTH;
@@ -128,8 +133,26 @@ sgemm_mfma_direct_kernel(GemmArgs g) {
   float* const As = lds;                                // [STAGES][A_STAGE]
   float* const Bs = lds + Cfg::STAGES * Cfg::A_STAGE;   // [STAGES][B_STAGE]
 
+  // Split K across workgroups: this workgroup's K range becomes the whole
+  // product of a narrower A and a shorter B, its tile goes to the partial
+  // buffer.  Everything below then reads g as for an unsplit product.
+  GemmArgs g = g_in;
   int tm, tn;
-  tile_of_workgroup(g, tm, tn);
+  if constexpr (SPLIT) {
+    int split;
+    tile_split_of_workgroup(g_in, tm, tn, split);
+    const int kb = split * g_in.k_split;
+    g.K = min(g_in.k_split, g_in.K - kb);
+    g.A = g_in.A + kb;
+    g.a_bytes = g_in.a_bytes - 4u * (uint32_t)kb;
+    g.B = g_in.B + (size_t)kb * (size_t)g_in.ldb;
+    g.b_bytes = g_in.b_bytes - 4u * (uint32_t)kb * (uint32_t)g_in.ldb;
+    g.C = g_in.W + (size_t)split * (size_t)g_in.M * (size_t)g_in.N;
+    g.ldc = g_in.N;
+    g.c_bytes = 4u * (uint32_t)g_in.M * (uint32_t)g_in.N;
+  } else {
+    tile_of_workgroup(g, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;

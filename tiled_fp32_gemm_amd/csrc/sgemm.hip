@@ -10,6 +10,7 @@
 #include "kernel_ladder.hpp"
 #include "kernel_mfma.hpp"
 #include "kernel_mfma_direct.hpp"
+#include "kernel_reduce.hpp"
 #include "kernel_simple.hpp"
 #include "kernel_transpose.hpp"
 
@@ -71,10 +72,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 typedef void (*KernelFn)(GemmArgs);
 typedef void (*KernelFnT)(sg::TransposeArgs);
+typedef void (*KernelFnR)(sg::ReduceArgs);
 
 struct Plan {
   sgemm_plan info;
   KernelFn fn;
+  int k_split;  // with info.splits > 1: K per split
 };
 
 bool vec_a_ok(const float* A, int64_t lda, int64_t K) {
@@ -89,6 +92,7 @@ struct Variant {
   const char* name;
   int tile_m, tile_n, tile_k, threads, lds_bytes;
   KernelFn vv, sv, vs, ss;  // by (A 128-bit?, B 128-bit?); null: unsupported
+  KernelFn split;           // the split-K-across-workgroups form, or null
 };
 
 template <int BM, int BN, int WM, int WN, int BK>
@@ -98,7 +102,7 @@ Variant reg_variant(const char* name) {
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, true, true>,
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, true>,
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, true, false>,
-          sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, false>};
+          sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, false>, nullptr};
 }
 
 // The LDS-direct kernel takes rows of any 4-byte alignment, so one kernel
@@ -107,7 +111,8 @@ template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KS>
 Variant direct_variant(const char* name) {
   using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, STAGES, KS>;
   const KernelFn f = sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES, KS>;
-  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, f, f, f, f};
+  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, f, f, f, f,
+          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES, KS, true>};
 }
 
 // Matrix-core configurations, large to small tiles, with the planner's two
@@ -167,9 +172,8 @@ constexpr double kWriteBW = 4.52e12;    // B/s: C stores of a final round
 // SIMD) and the latency of its loads; each round adds a fixed cost; and the
 // C tiles of the final round, which all CUs store at once, are charged at
 // the chip's write bandwidth.
-double estimate(const Candidate& c, int64_t M, int64_t N, int64_t K) {
+double estimate_grid(const Candidate& c, int64_t tiles, int64_t K) {
   const Variant& v = c.v;
-  const int64_t tiles = cdiv(M, v.tile_m) * cdiv(N, v.tile_n);
   const int64_t n = cdiv(tiles, kCUs);
   const int64_t slabs = K > v.tile_k ? cdiv(K, v.tile_k) : 1;
   const double waves = v.threads / 64.0;
@@ -188,8 +192,10 @@ double estimate(const Candidate& c, int64_t M, int64_t N, int64_t K) {
   return t;
 }
 
-// The candidate with the least estimated time; ties keep the earlier
-// (larger-tile) one.
+double estimate(const Candidate& c, int64_t M, int64_t N, int64_t K) {
+  return estimate_grid(c, cdiv(M, c.v.tile_m) * cdiv(N, c.v.tile_n), K);
+}
+
 const Candidate& choose_mfma(int64_t M, int64_t N, int64_t K, bool direct) {
   int n;
   const Candidate* c = mfma_candidates(direct, n);
@@ -205,6 +211,53 @@ const Candidate& choose_mfma(int64_t M, int64_t N, int64_t K, bool direct) {
   return c[best];
 }
 
+// Split K across workgroups, for grids that leave the chip under-filled:
+// S splits of k_split (a multiple of the slab) make S times the workgroups,
+// each over a K range of its own, into S partial tiles in the workspace; a
+// second pass adds them in split order.  Its cost: the partial products
+// (the model above, on tiles x S workgroups of depth k_split), plus the
+// reduction's (S + 1) M N 4 bytes at HBM speed and its launch.
+constexpr double kReduceFixed = 3.0e-6;  // s
+constexpr double kReduceBW = 5.0e12;     // B/s, a device copy's rate
+constexpr double kSplitMargin = 0.97;    // split only when clearly faster
+
+struct Choice {
+  const Candidate* c;
+  int splits, k_split;
+};
+
+Choice choose_direct(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
+  Choice best = {&choose_mfma(M, N, K, true), 1, 0};
+  const double t_one = estimate(*best.c, M, N, K);
+  if (ws_bytes <= 0 || M == 0 || N == 0 || K < 2) return best;
+  int n;
+  const Candidate* cs = mfma_candidates(true, n);
+  static const int kSplits[] = {2, 3, 4, 6, 8, 12, 16, 24, 32};
+  double t_best = 0;
+  Choice split = best;
+  for (int i = 0; i < n; ++i) {
+    const Candidate& c = cs[i];
+    const int64_t tiles = cdiv(M, c.v.tile_m) * cdiv(N, c.v.tile_n);
+    for (int S : kSplits) {
+      const int64_t ks = cdiv(cdiv(K, S), c.v.tile_k) * c.v.tile_k;
+      const int64_t se = cdiv(K, ks);  // splits actually used
+      if (se < 2) continue;
+      const int64_t bytes = se * M * N * 4;
+      if (bytes > ws_bytes || bytes >= kMaxOperandBytes) continue;
+      const double t = estimate_grid(c, tiles * se, ks) + kReduceFixed +
+                       (double)(se + 1) * M * N * 4.0 / kReduceBW;
+      if (split.splits == 1 || t < t_best) {
+        split = {&c, (int)se, (int)ks};
+        t_best = t;
+      }
+    }
+  }
+  if (split.splits > 1 && t_best < t_one * kSplitMargin) return split;
+  return best;
+}
+
+// The candidate with the least estimated time; ties keep the earlier
+// (larger-tile) one.
 KernelFn fma_fn(bool va, bool vb, bool vc) {
   const int idx = (va ? 4 : 0) | (vb ? 2 : 0) | (vc ? 1 : 0);
   static const KernelFn table[8] = {
@@ -223,9 +276,10 @@ void set_name(sgemm_plan& p, const char* base, bool va, bool vb) {
 // Chooses the kernel and fills the launch geometry for checked arguments.
 Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
               const float* B, int64_t ldb, const float* C, int64_t ldc,
-              int algo) {
+              int algo, int64_t ws_bytes = 0) {
   Plan p;
   memset(&p, 0, sizeof(p));
+  p.info.splits = 1;
   // With K == 0 neither A nor B is read, so any load form will do.
   const bool va = K == 0 || vec_a_ok(A, lda, K);
   const bool vb = K == 0 || vec_b_ok(B, ldb, N);
@@ -251,7 +305,10 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     p.fn = fma_fn(va, vb, vc);
     set_name(p.info, "fma_128x128x16", va, vb);
   } else {
-    const Candidate& cand = choose_mfma(M, N, K, algo == SGEMM_ALGO_MFMA_DIRECT);
+    Choice ch = {nullptr, 1, 0};
+    if (algo == SGEMM_ALGO_MFMA_DIRECT) ch = choose_direct(M, N, K, ws_bytes);
+    else ch.c = &choose_mfma(M, N, K, false);
+    const Candidate& cand = *ch.c;
     const Variant& v = cand.v;
     p.info.wg_per_cu = cand.occ;
     p.info.tile_m = v.tile_m;
@@ -259,11 +316,19 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     p.info.tile_k = v.tile_k;
     p.info.threads = v.threads;
     p.info.lds_bytes = v.lds_bytes;
-    p.fn = va ? (vb ? v.vv : v.vs) : (vb ? v.sv : v.ss);
-    set_name(p.info, v.name, va, vb);
+    if (ch.splits > 1) {
+      p.fn = v.split;
+      p.k_split = ch.k_split;
+      p.info.splits = ch.splits;
+      p.info.workspace_bytes = (int64_t)ch.splits * M * N * 4;
+      snprintf(p.info.kernel, sizeof(p.info.kernel), "%s_split%d", v.name, ch.splits);
+    } else {
+      p.fn = va ? (vb ? v.vv : v.vs) : (vb ? v.sv : v.ss);
+      set_name(p.info, v.name, va, vb);
+    }
   }
   p.info.workgroups = (M > 0 && N > 0)
-                          ? cdiv(M, p.info.tile_m) * cdiv(N, p.info.tile_n)
+                          ? cdiv(M, p.info.tile_m) * cdiv(N, p.info.tile_n) * p.info.splits
                           : 0;
   return p;
 }
@@ -273,7 +338,8 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
 int launch_gemm(KernelFn fn, int64_t M, int64_t N, int64_t K, const float* A,
                 int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                 const Checked& c, int tile_m, int tile_n, int threads,
-                hipStream_t stream) {
+                hipStream_t stream, int splits = 1, int k_split = 0,
+                float* W = nullptr) {
   GemmArgs g;
   g.A = A;
   g.B = B;
@@ -291,11 +357,41 @@ int launch_gemm(KernelFn fn, int64_t M, int64_t N, int64_t K, const float* A,
   g.tiles_m = (int)cdiv(M, tile_m);
   g.tiles_n = (int)cdiv(N, tile_n);
   g.group_m = g.tiles_m < 8 ? g.tiles_m : 8;
+  g.splits = splits;
+  g.k_split = k_split;
+  g.W = W;
 
   void* kargs[] = {&g};
   const hipError_t e = hipLaunchKernel(
       reinterpret_cast<const void*>(fn),
-      dim3((unsigned)((int64_t)g.tiles_m * g.tiles_n)), dim3(threads), kargs, 0, stream);
+      dim3((unsigned)((int64_t)g.tiles_m * g.tiles_n * splits)), dim3(threads), kargs, 0,
+      stream);
+  return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+// C = the sum of the splits partial products in W, in split order.
+int launch_reduce(const float* W, int splits, int64_t M, int64_t N, float* C,
+                  int64_t ldc, const Checked& c, hipStream_t stream) {
+  sg::ReduceArgs r;
+  r.W = W;
+  r.C = C;
+  r.w_bytes = (uint32_t)(splits * M * N * 4);
+  r.c_bytes = (uint32_t)c.c_bytes;
+  r.M = (int)M;
+  r.N = (int)N;
+  r.ldc = (int)(M > 1 ? ldc : (N > 1 ? N : 1));
+  r.splits = splits;
+  r.groups_per_row = (int)cdiv(N, 4);
+  const bool vw = aligned16(W) && N % 4 == 0;
+  const bool vc = vw && aligned16(C) && r.ldc % 4 == 0;
+  static const KernelFnR table[3] = {sg::sgemm_split_reduce_kernel<false, false>,
+                                     sg::sgemm_split_reduce_kernel<true, false>,
+                                     sg::sgemm_split_reduce_kernel<true, true>};
+  const KernelFnR fn = table[vc ? 2 : (vw ? 1 : 0)];
+  void* kargs[] = {&r};
+  const hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void*>(fn), dim3((unsigned)cdiv(M * r.groups_per_row, 256)),
+      dim3(256), kargs, 0, stream);
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
@@ -381,6 +477,51 @@ int sgemm_ladder(int step, int64_t M, int64_t N, int64_t K, const float* A,
   const bool vec = K == 0 || (vec_a_ok(A, lda, K) && vec_b_ok(B, ldb, N));
   return launch_gemm(vec ? ls.vec : ls.sca, M, N, K, A, lda, B, ldb, C, ldc, c,
                      ls.tile_m, ls.tile_n, 256, stream);
+}
+
+int sgemm_ws(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+             const float* B, int64_t ldb, float* C, int64_t ldc,
+             hipStream_t stream, void* workspace, int64_t workspace_bytes) {
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && workspace == nullptr) ||
+      ((uintptr_t)workspace & 3u))
+    return SGEMM_ERR_INVALID_ARG;
+  Checked c;
+  const int st = check(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_AUTO, c);
+  if (st != SGEMM_OK || !c.launch) return st;
+  const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_MFMA_DIRECT,
+                          workspace_bytes);
+  if (p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;
+  if (p.info.splits == 1)
+    return launch_gemm(p.fn, M, N, K, A, lda, B, ldb, C, ldc, c, p.info.tile_m,
+                       p.info.tile_n, p.info.threads, stream);
+  float* W = static_cast<float*>(workspace);
+  const int64_t wb = p.info.workspace_bytes;
+  if (overlaps(W, wb, A, c.a_bytes) || overlaps(W, wb, B, c.b_bytes) ||
+      overlaps(W, wb, C, c.c_bytes))
+    return SGEMM_ERR_INVALID_ARG;
+  const int e = launch_gemm(p.fn, M, N, K, A, lda, B, ldb, W, N, c, p.info.tile_m,
+                            p.info.tile_n, p.info.threads, stream, p.info.splits,
+                            p.k_split, W);
+  if (e != SGEMM_OK) return e;
+  return launch_reduce(W, p.info.splits, M, N, C, ldc, c, stream);
+}
+
+int64_t sgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < 0) return 0;
+  const Choice ch = choose_direct(M, N, K, kMaxOperandBytes);
+  return ch.splits > 1 ? (int64_t)ch.splits * M * N * 4 : 0;
+}
+
+int sgemm_plan_query_ws(int64_t M, int64_t N, int64_t K, const float* A,
+                        int64_t lda, const float* B, int64_t ldb, const float* C,
+                        int64_t ldc, int64_t workspace_bytes, sgemm_plan* plan) {
+  if (plan == nullptr || workspace_bytes < 0) return SGEMM_ERR_INVALID_ARG;
+  Checked c;
+  const int st = check(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_AUTO, c);
+  if (st != SGEMM_OK) return st;
+  *plan = plan_for(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_MFMA_DIRECT,
+                   workspace_bytes).info;
+  return SGEMM_OK;
 }
 
 int sgemm(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
