@@ -190,6 +190,38 @@ def test_power_of_two_scaling_is_exact(algo):
 
 
 @pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("M,N,K", [(1000, 1500, 777), (333, 517, 129)])
+def test_transposed_operands(algo, M, N, K):
+    """(A·B)^T = B^T·A^T: the product of the transposed operands (made on the
+    host) is the transpose of the product, within tolerance on random data
+    and bit for bit on integer data, where every order of the sum is exact.
+    The integer product is also transposed on the GPU by sgemm_transpose."""
+    import tiled_fp32_gemm_amd as sg
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 97)
+    dAt = DevMat(np.ascontiguousarray(A.T))
+    dBt = DevMat(np.ascontiguousarray(B.T))
+    dCt = DevMat(np.full((N, M), np.nan, np.float32))
+    say(f"[gpu] transposed operands {algo} {M}x{N}x{K}")
+    assert run(N, M, K, dBt, dAt, dCt, algo)
+    Cref, T = oracle.gemm(A, B)
+    assert_close(np.ascontiguousarray(dCt.host().T), Cref, T, f"(A.B)^T {algo}")
+
+    Ai = seedgen.integer_matrix(M, K, -8, 8, 98)
+    Bi = seedgen.integer_matrix(K, N, -8, 8, 98, start=M * K)
+    dA, dB = DevMat(Ai), DevMat(Bi)
+    dC = DevMat(np.full((M, N), np.nan, np.float32))
+    assert run(M, N, K, dA, dB, dC, algo)
+    dAt, dBt = DevMat(np.ascontiguousarray(Ai.T)), DevMat(np.ascontiguousarray(Bi.T))
+    assert run(N, M, K, dBt, dAt, dCt, algo)
+    dT = DevMat(np.full((N, M), np.nan, np.float32))
+    assert sg.sgemm_transpose(M, N, dC.ptr, N, dT.ptr, M,
+                              torch.cuda.current_stream().cuda_stream) == sg.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(dT.host(), dCt.host())
+    assert np.array_equal(dC.host(), oracle.gemm(Ai, Bi, with_t=False)[0].astype(np.float32))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
 def test_k_zero_writes_zeros_and_empty_is_noop(algo):
     import tiled_fp32_gemm_amd as sg
     M, N = 70, 90

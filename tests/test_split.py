@@ -205,3 +205,23 @@ def test_repeated_calls_with_a_shared_workspace():
         run_ws(M, N, K, dA, dB, dC, ws)
         Cref, T = oracle.gemm(A, B)
         assert_close(dC.host(), Cref, T, f"shared ws {M}x{N}x{K}")
+
+
+def test_split_power_of_two_scaling_is_exact():
+    """C(2A) = 2 C(A) and C(A/4) = C(A)/4 bit for bit through the split
+    path: scaling by a power of two commutes with every rounding of both
+    passes."""
+    import tiled_fp32_gemm_amd as sg
+    M, N, K = 256, 256, 8192
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 89)
+    dB = DevMat(B)
+    ws = Workspace(sg.sgemm_workspace_bytes(M, N, K))
+    res = []
+    for scale in (1.0, 2.0, 0.25):
+        dA = DevMat((A * np.float32(scale)).astype(np.float32))
+        dC = DevMat(np.full((M, N), np.nan, np.float32))
+        say(f"[gpu] split scaling x{scale}")
+        run_ws(M, N, K, dA, dB, dC, ws)
+        res.append(dC.host())
+    assert np.array_equal(res[1], 2.0 * res[0])
+    assert np.array_equal(res[2], 0.25 * res[0])
