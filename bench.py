@@ -4,8 +4,10 @@
 A step is one product over the workload (default: M = N = K = 4096,
 row-major, A and B uniform on [-1, 1) from seed 2) with A, B and C resident in
 HBM.  W untimed steps, then K timed steps bracketed by device
-synchronisation; each launch is also bracketed by HIP events on the stream it
-is enqueued on.  Prints one JSON line.
+synchronisation.  Every --event-every-th launch of the timed steps is also
+bracketed by a pair of HIP events on the stream it is enqueued on (each pair
+adds a few microseconds between kernels, so they are not put around every
+launch).  Prints one JSON line.
 
   value            2MNK * K / wall time of the K steps, TFLOP/s
   roofline         the GEMM kernel against the FP32 matrix peak (157.3
@@ -171,7 +173,8 @@ def bench_transpose(args) -> int:
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"transpose {rows}x{cols} fp32, layout {args.layout}",
                    "buffer_pairs": n,
-                   "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+                   "event_timed_launches": len(timed),
+            "kernel_ms_median": round(float(np.median(ev_ms)), 5),
                    "copy_same_bytes_gbs": round(copy_gbs, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -234,7 +237,8 @@ def bench_ladder(args) -> int:
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": f"sgemm {args.workload}: M={M} N={N} K={K}",
                        "ladder_step": step, "name": name,
-                       "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+                       "event_timed_launches": len(timed),
+            "kernel_ms_median": round(float(np.median(ev_ms)), 5),
                        "max_rel_diff_vs_sgemm": rel},
             "roofline": {"bound": "mfma" if name.startswith("mfma") else "alu",
                          "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
@@ -258,6 +262,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle sample until this much time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=10, metavar="N",
+                    help="time every N-th launch of the timed steps with HIP events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--op", default="sgemm", choices=["sgemm", "transpose"])
     ap.add_argument("--ladder", action="store_true",
@@ -316,17 +322,22 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    timed = [i for i in range(args.steps) if i % every == every // 2] or [0]
+    starts = {i: torch.cuda.Event(enable_timing=True) for i in timed}
+    ends = {i: torch.cuda.Event(enable_timing=True) for i in timed}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
+        if i in starts:
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        else:
+            step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ev_ms = np.array([starts[i].elapsed_time(ends[i]) for i in timed])
 
     flops = 2.0 * M * N * K
     value = flops * args.steps / wall / 1e12
@@ -358,6 +369,7 @@ def main() -> int:
             "workgroups": plan["workgroups"],
             "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
             "compulsory_hbm_gbs": round(compulsory / kern_s / 1e9, 1),
+            "event_timed_launches": len(timed),
             "kernel_ms_median": round(float(np.median(ev_ms)), 5),
             "kernel_ms_p10_p90": [round(float(np.percentile(ev_ms, 10)), 5),
                                   round(float(np.percentile(ev_ms, 90)), 5)],
