@@ -22,6 +22,10 @@ launch).  Prints one JSON line.
 ``--ladder`` runs every step of the ablation ladder (``sgemm_ladder``) on the
 workload instead, one JSON line per step.
 
+``--op sgemm_ws`` times ``sgemm_ws`` (K split across workgroups through a
+workspace of ``sgemm_workspace_bytes``) on the workload, with the plain
+``sgemm`` of the same shape beside it; the events bracket both of its kernels.
+
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
 the counter scale factors) and prints its size.  ``--op transpose`` measures
 the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s,
@@ -51,6 +55,9 @@ WORKLOADS = {
     "ragged": (1000, 1500, 777, "uniform", 3),
     "skinny": (65536, 128, 256, "normal", 4),
     "8192cube": (8192, 8192, 8192, "normal", 5),
+    # under-filled grids with a long K, for --op sgemm_ws (split K)
+    "256x256x8192": (256, 256, 8192, "uniform", 6),
+    "512x512x16384": (512, 512, 16384, "normal", 7),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.txt")
 
@@ -173,12 +180,103 @@ def bench_transpose(args) -> int:
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"transpose {rows}x{cols} fp32, layout {args.layout}",
                    "buffer_pairs": n,
-                   "event_timed_launches": len(timed),
-            "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+                   "kernel_ms_median": round(float(np.median(ev_ms)), 5),
                    "copy_same_bytes_gbs": round(copy_gbs, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
+def timed_steps(step, steps: int, warmup: int, every: int, stream):
+    """Runs warmup untimed steps, then steps timed ones between two device
+    synchronisations, every every-th also between two HIP events on stream.
+    Returns (wall seconds, event-timed milliseconds of the sampled steps)."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    every = max(1, every)
+    timed = [i for i in range(steps) if i % every == every // 2] or [0]
+    starts = {i: torch.cuda.Event(enable_timing=True) for i in timed}
+    ends = {i: torch.cuda.Event(enable_timing=True) for i in timed}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i in starts:
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        else:
+            step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, np.array([starts[i].elapsed_time(ends[i]) for i in timed])
+
+
+def bench_ws(args) -> int:
+    """sgemm_ws on the workload (two kernels per step: the partial products of
+    the K splits, then their fixed-order sum), with plain sgemm beside it."""
+    import numpy as np
+    import torch
+
+    import seedgen
+    import tiled_fp32_gemm_amd as sg
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sg.load()
+    M, N, K, dist, seed = WORKLOADS[args.workload]
+    A, B = seedgen.gemm_inputs(M, N, K, dist, seed)
+    dev = torch.device("cuda:0")
+    tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    tC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    need = sg.sgemm_workspace_bytes(M, N, K)
+    ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=dev)
+    st, plan = sg.sgemm_plan_query_ws(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
+                                      tC.data_ptr(), N, need)
+    if st != sg.OK:
+        raise sg.SgemmError(st, "sgemm_plan_query_ws")
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step_ws():
+        st = sg.sgemm_ws(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(),
+                         N, sh, ws.data_ptr(), need)
+        if st != sg.OK:
+            raise sg.SgemmError(st, "sgemm_ws")
+
+    def step_plain():
+        st = sg.sgemm(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N, sh)
+        if st != sg.OK:
+            raise sg.SgemmError(st, "sgemm")
+
+    wall, ev_ms = timed_steps(step_ws, args.steps, args.warmup, args.event_every, stream)
+    wall_p, ev_p = timed_steps(step_plain, args.steps, args.warmup, args.event_every,
+                               stream)
+    flops = 2.0 * M * N * K
+    achieved = flops / (float(ev_ms.mean()) / 1e3) / 1e12
+    print(json.dumps({
+        "metric": "SGEMM TFLOP/s with K split across workgroups (fp32, 1 GPU)",
+        "value": round(flops * args.steps / wall / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"sgemm_ws {args.workload}: C=A·B, M={M} N={N} "
+                               f"K={K}, row-major fp32, A,B {dist} seed {seed}",
+                   "M": M, "N": N, "K": K, "kernel": plan.kernel.decode(),
+                   "splits": plan.splits, "workspace_bytes": plan.workspace_bytes,
+                   "workgroups": plan.workgroups,
+                   "event_timed_launches": len(ev_ms),
+                   "call_ms_median": round(float(np.median(ev_ms)), 5),
+                   "sgemm_same_shape_tflops": round(flops * args.steps / wall_p / 1e12, 3),
+                   "sgemm_same_shape_ms_median": round(float(np.median(ev_p)), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None},
         "cpu_baseline": None}), flush=True)
     return 0
 
@@ -237,8 +335,7 @@ def bench_ladder(args) -> int:
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": f"sgemm {args.workload}: M={M} N={N} K={K}",
                        "ladder_step": step, "name": name,
-                       "event_timed_launches": len(timed),
-            "kernel_ms_median": round(float(np.median(ev_ms)), 5),
+                       "kernel_ms_median": round(float(np.median(ev_ms)), 5),
                        "max_rel_diff_vs_sgemm": rel},
             "roofline": {"bound": "mfma" if name.startswith("mfma") else "alu",
                          "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
@@ -265,7 +362,7 @@ def main() -> int:
     ap.add_argument("--event-every", type=int, default=10, metavar="N",
                     help="time every N-th launch of the timed steps with HIP events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--op", default="sgemm", choices=["sgemm", "transpose"])
+    ap.add_argument("--op", default="sgemm", choices=["sgemm", "sgemm_ws", "transpose"])
     ap.add_argument("--ladder", action="store_true",
                     help="run every ablation ladder step on the workload")
     ap.add_argument("--layout", default="auto",
@@ -293,6 +390,8 @@ def main() -> int:
         return 0
     if args.op == "transpose":
         return bench_transpose(args)
+    if args.op == "sgemm_ws":
+        return bench_ws(args)
     if args.ladder:
         return bench_ladder(args)
 
@@ -318,26 +417,7 @@ def main() -> int:
         if st != sg.OK:
             raise sg.SgemmError(st, "sgemm_ex")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    every = max(1, args.event_every)
-    timed = [i for i in range(args.steps) if i % every == every // 2] or [0]
-    starts = {i: torch.cuda.Event(enable_timing=True) for i in timed}
-    ends = {i: torch.cuda.Event(enable_timing=True) for i in timed}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i in starts:
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-        else:
-            step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = np.array([starts[i].elapsed_time(ends[i]) for i in timed])
+    wall, ev_ms = timed_steps(step, args.steps, args.warmup, args.event_every, stream)
 
     flops = 2.0 * M * N * K
     value = flops * args.steps / wall / 1e12
@@ -369,7 +449,7 @@ def main() -> int:
             "workgroups": plan["workgroups"],
             "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
             "compulsory_hbm_gbs": round(compulsory / kern_s / 1e9, 1),
-            "event_timed_launches": len(timed),
+            "event_timed_launches": len(ev_ms),
             "kernel_ms_median": round(float(np.median(ev_ms)), 5),
             "kernel_ms_p10_p90": [round(float(np.percentile(ev_ms, 10)), 5),
                                   round(float(np.percentile(ev_ms, 90)), 5)],
