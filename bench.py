@@ -3,11 +3,15 @@
 
 A step is one product over the workload (default: M = N = K = 4096,
 row-major, A and B uniform on [-1, 1) from seed 2) with A, B and C resident in
-HBM.  W untimed steps, then K timed steps bracketed by device
-synchronisation.  Every --event-every-th launch of the timed steps is also
-bracketed by a pair of HIP events on the stream it is enqueued on (each pair
-adds a few microseconds between kernels, so they are not put around every
-launch).  Prints one JSON line.
+HBM.  For the skinny workload, whose operands would fit in the 256 MiB
+last-level cache, the steps rotate over three operand sets (``--buffers``).
+
+W untimed steps (by default as many as take 0.3 s, at least 20: an idle GPU
+needs tens of milliseconds of work to reach its full clock), then K timed
+steps bracketed by device synchronisation.  Every --event-every-th launch of
+the timed steps is also bracketed by a pair of HIP events on the stream it is
+enqueued on (each pair adds a few microseconds between kernels, so they are
+not put around every launch).  Prints one JSON line.
 
   value            2MNK * K / wall time of the K steps, TFLOP/s
   roofline         the GEMM kernel against the FP32 matrix peak (157.3
@@ -137,7 +141,7 @@ def bench_transpose(args) -> int:
     g.manual_seed(7)
     # Launch i uses buffer pair i mod n: with n pairs spanning more than the
     # 256 MiB last-level cache, every launch reads and writes HBM.
-    n = max(1, args.buffers)
+    n = max(1, 4 if args.buffers is None else args.buffers)
     tins = [torch.rand((rows, cols), device=dev, generator=g) for _ in range(n)]
     touts = [torch.empty((cols, rows), device=dev) for _ in range(n)]
     stream = torch.cuda.current_stream(dev)
@@ -151,8 +155,7 @@ def bench_transpose(args) -> int:
             raise sg.SgemmError(st, "sgemm_transpose_ex")
 
     def timed(fn):
-        for i in range(args.warmup):
-            fn(i)
+        timed.nwarm = warm_up(fn, args)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -166,6 +169,7 @@ def bench_transpose(args) -> int:
         return wall, np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
 
     wall, ev_ms = timed(step)
+    nwarm = timed.nwarm
     # Context: a device-to-device copy of the same bytes over the same buffers.
     _, copy_ms = timed(lambda i: touts[i % n].view(-1).copy_(tins[i % n].view(-1)))
     nbytes = 2.0 * 4 * rows * cols
@@ -174,7 +178,7 @@ def bench_transpose(args) -> int:
     print(json.dumps({
         "metric": "tiled transpose GB/s (fp32, 1 GPU)",
         "value": round(nbytes * args.steps / wall / 1e9, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": nwarm,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
@@ -189,15 +193,35 @@ def bench_transpose(args) -> int:
     return 0
 
 
-def timed_steps(step, steps: int, warmup: int, every: int, stream):
-    """Runs warmup untimed steps, then steps timed ones between two device
-    synchronisations, every every-th also between two HIP events on stream.
-    Returns (wall seconds, event-timed milliseconds of the sampled steps)."""
+def warm_up(fn, args) -> int:
+    """Untimed steps fn(0), fn(1), ...: exactly --warmup of them when given;
+    by default at least 20 and at least --warmup-seconds of device time, in
+    synchronised batches of 10, since an idle GPU takes tens of
+    milliseconds of work to reach its full clock.  Returns the count."""
+    import torch
+    if args.warmup is not None:
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        return args.warmup
+    n, t0 = 0, time.perf_counter()
+    while n < 20 or time.perf_counter() - t0 < args.warmup_seconds:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def timed_steps(step, args, stream):
+    """Warms up (warm_up), then runs --steps timed steps between two device
+    synchronisations, every --event-every-th also between two HIP events on
+    stream.  Returns (wall seconds, event-timed milliseconds of the sampled
+    steps, warm-up steps)."""
     import numpy as np
     import torch
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(lambda i: step(), args)
+    steps, every = args.steps, args.event_every
     every = max(1, every)
     timed = [i for i in range(steps) if i % every == every // 2] or [0]
     starts = {i: torch.cuda.Event(enable_timing=True) for i in timed}
@@ -213,7 +237,7 @@ def timed_steps(step, steps: int, warmup: int, every: int, stream):
             step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, np.array([starts[i].elapsed_time(ends[i]) for i in timed])
+    return wall, np.array([starts[i].elapsed_time(ends[i]) for i in timed]), nwarm
 
 
 def bench_ws(args) -> int:
@@ -253,15 +277,14 @@ def bench_ws(args) -> int:
         if st != sg.OK:
             raise sg.SgemmError(st, "sgemm")
 
-    wall, ev_ms = timed_steps(step_ws, args.steps, args.warmup, args.event_every, stream)
-    wall_p, ev_p = timed_steps(step_plain, args.steps, args.warmup, args.event_every,
-                               stream)
+    wall, ev_ms, nwarm = timed_steps(step_ws, args, stream)
+    wall_p, ev_p, _ = timed_steps(step_plain, args, stream)
     flops = 2.0 * M * N * K
     achieved = flops / (float(ev_ms.mean()) / 1e3) / 1e12
     print(json.dumps({
         "metric": "SGEMM TFLOP/s with K split across workgroups (fp32, 1 GPU)",
         "value": round(flops * args.steps / wall / 1e12, 3), "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": nwarm,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
@@ -310,8 +333,7 @@ def bench_ladder(args) -> int:
                                  tC.data_ptr(), N, sh)
             if st != sg.OK:
                 raise sg.SgemmError(st, "sgemm_ladder")
-        for _ in range(args.warmup):
-            run()
+        nwarm = warm_up(lambda i: run(), args)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -329,7 +351,7 @@ def bench_ladder(args) -> int:
         print(json.dumps({
             "metric": "ablation ladder step TFLOP/s (fp32, 1 GPU)",
             "value": round(flops * args.steps / wall / 1e12, 3), "unit": "TFLOP/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "n_gpus": 1, "steps": args.steps, "warmup": nwarm,
             "ms_per_step": round(wall / args.steps * 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
@@ -351,7 +373,10 @@ def main() -> int:
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default: at least 20 and at least "
+                         "--warmup-seconds of device time)")
+    ap.add_argument("--warmup-seconds", type=float, default=0.3)
     ap.add_argument("--workload", default="4096cube", choices=sorted(WORKLOADS))
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "simple"])
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -367,8 +392,10 @@ def main() -> int:
                     help="run every ablation ladder step on the workload")
     ap.add_argument("--layout", default="auto",
                     choices=["auto", "naive", "padded", "swizzled"])
-    ap.add_argument("--buffers", type=int, default=4,
-                    help="transpose: buffer pairs the launches rotate over")
+    ap.add_argument("--buffers", type=int, default=None,
+                    help="operand sets the launches rotate over (transpose: "
+                         "4 pairs; sgemm: 3 for skinny, whose set is smaller "
+                         "than the 256 MiB last-level cache, else 1)")
     ap.add_argument("--rows", type=int, default=8192)
     ap.add_argument("--cols", type=int, default=8192)
     args = ap.parse_args()
@@ -403,21 +430,33 @@ def main() -> int:
     M, N, K, dist, seed = WORKLOADS[args.workload]
     A, B = seedgen.gemm_inputs(M, N, K, dist, seed)
     dev = torch.device("cuda:0")
+    # Step i uses operand set i mod n.  Set 0 holds the seeded inputs; the
+    # others are copies at other addresses, so that with n sets spanning more
+    # than the last-level cache no launch finds its operands there.
+    nsets = args.buffers if args.buffers is not None else (
+        3 if args.workload == "skinny" else 1)
+    nsets = max(1, nsets)
     tA = torch.from_numpy(A).to(dev)
     tB = torch.from_numpy(B).to(dev)
-    tC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    sets = [(tA, tB, torch.empty((M, N), dtype=torch.float32, device=dev))]
+    for _ in range(nsets - 1):
+        sets.append((tA.clone(), tB.clone(), torch.empty_like(sets[0][2])))
+    tC = sets[0][2]
     algo = sg.ALGOS[args.algo]
     plan = sg.plan(tA, tB, tC, algo)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in sets]
+    counter = [0]
 
     def step():
-        st = sg.sgemm_ex(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
-                         tC.data_ptr(), N, sh, algo)
+        pa, pb, pc = ptrs[counter[0] % nsets]
+        counter[0] += 1
+        st = sg.sgemm_ex(M, N, K, pa, K, pb, N, pc, N, sh, algo)
         if st != sg.OK:
             raise sg.SgemmError(st, "sgemm_ex")
 
-    wall, ev_ms = timed_steps(step, args.steps, args.warmup, args.event_every, stream)
+    wall, ev_ms, nwarm = timed_steps(step, args, stream)
 
     flops = 2.0 * M * N * K
     value = flops * args.steps / wall / 1e12
@@ -433,7 +472,7 @@ def main() -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -447,6 +486,7 @@ def main() -> int:
             "kernel": plan["kernel"], "tile": [plan["tile_m"], plan["tile_n"],
                                                 plan["tile_k"]],
             "workgroups": plan["workgroups"],
+            "operand_sets": nsets,
             "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
             "compulsory_hbm_gbs": round(compulsory / kern_s / 1e9, 1),
             "event_timed_launches": len(ev_ms),

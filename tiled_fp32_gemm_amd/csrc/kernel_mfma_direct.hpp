@@ -8,19 +8,29 @@
 // to padding); here it removes the staging registers and the LDS store
 // instructions and keeps STAGES - 1 slabs in flight.
 //
-// Alignment.  The load-to-LDS form takes 16 bytes from any 4-byte-aligned
-// address and range-checks each 4-byte word against the resource, so rows of
-// any alignment and leading dimension are loaded as whole 4-float groups:
+// Alignment and edges.  The load-to-LDS form takes 16 bytes from any
+// 4-byte-aligned address and range-checks each 4-byte word against the
+// resource, so rows of any alignment and leading dimension are loaded as
+// whole 4-float groups.  A lane's offset inside a slab never changes: each
+// slab moves the two resources instead (A's base by k0 columns, B's by k0
+// rows, their sizes shrunk to match), so a load is one instruction with no
+// per-lane address arithmetic.  The range check then does the edges:
+//   * A groups of rows >= M and B groups starting at a column >= N get the
+//     offset kOob once, and read zeros in every slab;
+//   * B rows k >= K lie past the end of the moved B resource and read zeros;
 //   * a B group reaching past column N-1 brings in values that only feed C
 //     columns >= N, which are never stored;
-//   * an A group reaching past row M-1 feeds only C rows >= M;
-//   * an A group that straddles k = K (possible in the last slab when K is
-//     not a multiple of 4) would bring in values from beyond the row, which
-//     meet the zero-filled B rows k >= K but could be NaN or Inf (a padding
-//     column, for instance): the lane that loaded such a group overwrites
-//     its words k >= K with 0 in LDS before the slab's barrier.  This is the
-//     pages' rule that an edge writes 0 for invalid elements ("CUDA in depth
-//     (5)", section on edges).
+//   * A words at k >= K of a row below M-1 are inside the allocation (the
+//     next row, a padding column that may hold NaN or Inf): in the last slab,
+//     when it is partial, the lane that loaded such a group overwrites those
+//     words with 0 in LDS before the slab's barrier.  This is the pages' rule
+//     that an edge writes 0 for invalid elements ("CUDA in depth (5)",
+//     section on edges).
+// The slabs after the last are loaded too, into stages no one reads again
+// (their resources are empty, so they read zeros): the loads between the
+// matrix instructions need no branch and every wait count is the same in
+// every step.  Their landing is awaited before the tile's LDS is reused or
+// released.
 //
 // A direct load writes lane l's 16 bytes at base + 16 l, so each layout is
 // chosen as a permutation of 16-byte units that keeps every load instruction
@@ -162,52 +172,56 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   const int wn0 = (sw % Cfg::WAVES_N) * WN;
   const int li = lane & 31, lh = lane >> 5;
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
 
-  // Unit u = s NT + 64 wave + lane of each load instruction, and the global
-  // 4-float group it takes.
+  // Unit u = s NT + 64 wave + lane of each load instruction, and the offset
+  // of the global 4-float group it takes in slab 0 (kOob when outside the
+  // matrix in M or N).
   uint32_t a_off[Cfg::A_SLOTS];
-  bool a_row_ok[Cfg::A_SLOTS];
-  int a_k[Cfg::A_SLOTS];
+  int a_k[Cfg::A_SLOTS];   // k of the group in its slab; 1 << 30 for rows >= M
 #pragma unroll
   for (int s = 0; s < Cfg::A_SLOTS; ++s) {
     const int u = s * NT + 64 * wave + lane;
     const int row = (u / (16 * CPR)) * 16 + (u & 15), c = (u >> 4) % CPR;
-    a_row_ok[s] = (m0 + row) < g.M;
-    a_k[s] = 4 * c;
-    a_off[s] = ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u;
+    const bool ok = (m0 + row) < g.M;
+    a_k[s] = ok ? 4 * c : 1 << 30;
+    a_off[s] = ok ? ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u : kOob;
   }
   uint32_t b_off[Cfg::B_SLOTS];
-  bool b_col_ok[Cfg::B_SLOTS];
-  int b_k[Cfg::B_SLOTS];
 #pragma unroll
   for (int s = 0; s < Cfg::B_SLOTS; ++s) {
     const int u = s * NT + 64 * wave + lane;
     const int k = u / QB, q = (u % QB) ^ ((k & 8) ? 8 : 0);
-    b_k[s] = k;
-    b_col_ok[s] = (n0 + 4 * q) < g.N;
-    b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u;
+    b_off[s] = (n0 + 4 * q) < g.N
+                   ? ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u
+                   : kOob;
   }
+  // The resources of the slab starting at k0 (64-bit shifts: past the end a
+  // slab's shift of B can exceed 32 bits; an empty resource reads zeros).
+  auto rsrc_a = [&](int k0) {
+    const uint64_t sh = 4ull * (uint64_t)k0;
+    return make_rsrc(g.A + k0, g.a_bytes > sh ? (uint32_t)(g.a_bytes - sh) : 0u);
+  };
+  auto rsrc_b = [&](int k0) {
+    const uint64_t sh = 4ull * (uint64_t)k0 * (uint64_t)g.ldb;
+    return make_rsrc(g.B + (size_t)k0 * (size_t)g.ldb,
+                     g.b_bytes > sh ? (uint32_t)(g.b_bytes - sh) : 0u);
+  };
 
   // Issue direct load l (the A slots, then the B slots) of the slab starting
-  // at k0 into stage st.  A group is loaded when its first element is inside
-  // the matrix.
+  // at k0 into stage st.
   auto issue_one = [&](int l, int k0, int st) {
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
       if (l != s) continue;
       float* dst = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave);
-      const bool ok = a_row_ok[s] && (k0 + a_k[s]) < g.K;
-      load4_to_lds(ra, dst, ok ? a_off[s] + (uint32_t)k0 * 4u : kOob);
+      load4_to_lds(rsrc_a(k0), dst, a_off[s]);
     }
 #pragma unroll
     for (int s = 0; s < Cfg::B_SLOTS; ++s) {
       if (l != Cfg::A_SLOTS + s) continue;
       float* dst = Bs + st * Cfg::B_STAGE + 4 * (s * NT + 64 * wave);
-      const bool ok = b_col_ok[s] && (k0 + b_k[s]) < g.K;
-      load4_to_lds(rb, dst, ok ? b_off[s] + (uint32_t)k0 * (uint32_t)g.ldb * 4u : kOob);
+      load4_to_lds(rsrc_b(k0), dst, b_off[s]);
     }
   };
   auto issue = [&](int k0, int st) {
@@ -229,23 +243,21 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nslab = (g.K + BK - 1) / BK;
-  const bool k_ragged = (g.K & 3) != 0;  // an A group straddles k = K
+  const bool k_tail = g.K % BK != 0;  // the last slab reaches past k = K
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nslab) issue(d * BK, d);
+  for (int d = 0; d < DEPTH; ++d) issue(d * BK, d);
 
   int st = 0;  // stage of slab t
   for (int t = 0; t < nslab; ++t) {
-    const int ahead = min(DEPTH - 1, nslab - 1 - t);  // later slabs in flight
-    wait_slabs<Cfg::LOADS, DEPTH>(ahead);
-    if (k_ragged && t == nslab - 1) {
-      // Zero this lane's own words k >= K of the straddling A group.
+    wait_slabs<Cfg::LOADS, DEPTH>(DEPTH - 1);  // later slabs stay in flight
+    if (k_tail && t == nslab - 1) {
+      // Zero this lane's own A words at k >= K (rows >= M read zeros).
 #pragma unroll
       for (int s = 0; s < Cfg::A_SLOTS; ++s) {
         const int k = t * BK + a_k[s];
-        if (a_row_ok[s] && k < g.K && g.K < k + 4) {
+        if (k + 4 > g.K && k < (1 << 29)) {
           float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + lane);
-          for (int e = g.K - k; e < 4; ++e) unit[e] = 0.0f;
+          for (int e = k < g.K ? g.K - k : 0; e < 4; ++e) unit[e] = 0.0f;
         }
       }
       __builtin_amdgcn_s_waitcnt(kLdsWait);
@@ -255,9 +267,8 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     // moving LDS accesses across it.  (A full __syncthreads() fence would
     // also wait for the later slabs, which must stay in flight.)
     asm volatile("s_barrier" ::: "memory");
-    const bool more = t + DEPTH < nslab;
     const int nk0 = (t + DEPTH) * BK, nst = st == 0 ? STAGES - 1 : st - 1;
-    if (!kSpread && more) issue(nk0, nst);
+    if (!kSpread) issue(nk0, nst);
 
     const float* as = As + st * Cfg::A_STAGE;
     const float* bs = Bs + st * Cfg::B_STAGE;
@@ -290,7 +301,7 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
         if (kSpread && uu == 0) {
 #pragma unroll
           for (int l = 0; l < Cfg::LOADS; ++l)
-            if (p == l * 8 / Cfg::LOADS && more) issue_one(l, nk0, nst);
+            if (p == l * 8 / Cfg::LOADS) issue_one(l, nk0, nst);
         }
 #pragma unroll
         for (int i = 0; i < TA; ++i)
@@ -302,6 +313,9 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     }
     st = (st == STAGES - 1) ? 0 : st + 1;
   }
+  // The loads of the slabs after the last land before the stages are reused
+  // (split-K sum) or the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
 
   if constexpr (KS > 1) {
     // Groups 1..KS-1 leave their partial tiles in LDS (lane-contiguous, so
