@@ -26,11 +26,9 @@
 //     words with 0 in LDS before the slab's barrier.  This is the pages' rule
 //     that an edge writes 0 for invalid elements ("CUDA in depth (5)",
 //     section on edges).
-// The slabs after the last are loaded too, into stages no one reads again
-// (their resources are empty, so they read zeros): the loads between the
-// matrix instructions need no branch and every wait count is the same in
-// every step.  Their landing is awaited before the tile's LDS is reused or
-// released.
+// The last STAGES - 1 slabs, which load nothing, are peeled off the main
+// loop, so the loads between the matrix instructions need no branch and
+// every wait count in the loop is the same.
 //
 // A direct load writes lane l's 16 bytes at base + 16 l, so each layout is
 // chosen as a permutation of 16-byte units that keeps every load instruction
@@ -70,6 +68,8 @@
 // range of k_split values of K into a partial buffer; sgemm_split_reduce
 // (kernel_reduce.hpp) then adds the partials in split order.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -196,37 +196,39 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
                    ? ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u
                    : kOob;
   }
-  // The resources of the slab starting at k0 (64-bit shifts: past the end a
-  // slab's shift of B can exceed 32 bits; an empty resource reads zeros).
+  // The resources of the slab starting at k0: A moved by k0 columns, B by
+  // k0 rows, each size shrunk to match.  Below K the shifts are smaller than
+  // the (sub-2 GiB) sizes, so 32-bit scalar arithmetic suffices; from K on
+  // the resource is empty and reads zeros.
   auto rsrc_a = [&](int k0) {
-    const uint64_t sh = 4ull * (uint64_t)k0;
-    return make_rsrc(g.A + k0, g.a_bytes > sh ? (uint32_t)(g.a_bytes - sh) : 0u);
+    const bool in = k0 < g.K;
+    return make_rsrc(in ? g.A + k0 : g.A, in ? g.a_bytes - 4u * (uint32_t)k0 : 0u);
   };
   auto rsrc_b = [&](int k0) {
-    const uint64_t sh = 4ull * (uint64_t)k0 * (uint64_t)g.ldb;
-    return make_rsrc(g.B + (size_t)k0 * (size_t)g.ldb,
-                     g.b_bytes > sh ? (uint32_t)(g.b_bytes - sh) : 0u);
+    const bool in = k0 < g.K;
+    const uint32_t sh = 4u * (uint32_t)k0 * (uint32_t)g.ldb;
+    return make_rsrc(in ? g.B + (size_t)(sh >> 2) : g.B, in ? g.b_bytes - sh : 0u);
   };
 
-  // Issue direct load l (the A slots, then the B slots) of the slab starting
-  // at k0 into stage st.
-  auto issue_one = [&](int l, int k0, int st) {
+  // Issue direct load l (the A slots, then the B slots) of a slab with
+  // resources (qa, qb) into stage st.
+  auto issue_one = [&](int l, __amdgpu_buffer_rsrc_t qa, __amdgpu_buffer_rsrc_t qb, int st) {
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
       if (l != s) continue;
       float* dst = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave);
-      load4_to_lds(rsrc_a(k0), dst, a_off[s]);
+      load4_to_lds(qa, dst, a_off[s]);
     }
 #pragma unroll
     for (int s = 0; s < Cfg::B_SLOTS; ++s) {
       if (l != Cfg::A_SLOTS + s) continue;
       float* dst = Bs + st * Cfg::B_STAGE + 4 * (s * NT + 64 * wave);
-      load4_to_lds(rsrc_b(k0), dst, b_off[s]);
+      load4_to_lds(qb, dst, b_off[s]);
     }
   };
-  auto issue = [&](int k0, int st) {
+  auto issue = [&](__amdgpu_buffer_rsrc_t qa, __amdgpu_buffer_rsrc_t qb, int st) {
 #pragma unroll
-    for (int l = 0; l < Cfg::LOADS; ++l) issue_one(l, k0, st);
+    for (int l = 0; l < Cfg::LOADS; ++l) issue_one(l, qa, qb, st);
   };
 
   // Spread the loads only where a slab's compute is long (one wave group):
@@ -245,30 +247,41 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   const int nslab = (g.K + BK - 1) / BK;
   const bool k_tail = g.K % BK != 0;  // the last slab reaches past k = K
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue(d * BK, d);
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nslab) issue(rsrc_a(d * BK), rsrc_b(d * BK), d);
 
-  int st = 0;  // stage of slab t
-  for (int t = 0; t < nslab; ++t) {
-    wait_slabs<Cfg::LOADS, DEPTH>(DEPTH - 1);  // later slabs stay in flight
-    if (k_tail && t == nslab - 1) {
-      // Zero this lane's own A words at k >= K (rows >= M read zeros).
+  // One slab: wait for its loads, publish it with the barrier, issue slab
+  // t + DEPTH's loads (LOADS, a compile-time flag) and compute.  The slabs
+  // that load are one loop with no branch among their matrix instructions;
+  // the last DEPTH slabs, which load nothing, follow it.
+  auto slab = [&](int t, int st, auto loads) {
+    constexpr bool kLoads = decltype(loads)::value;
+    if constexpr (kLoads) {
+      wait_slabs<Cfg::LOADS, DEPTH>(DEPTH - 1);  // later slabs stay in flight
+    } else {
+      wait_slabs<Cfg::LOADS, DEPTH>(min(DEPTH - 1, nslab - 1 - t));
+      if (k_tail && t == nslab - 1) {
+        // Zero this lane's own A words at k >= K (rows >= M read zeros).
 #pragma unroll
-      for (int s = 0; s < Cfg::A_SLOTS; ++s) {
-        const int k = t * BK + a_k[s];
-        if (k + 4 > g.K && k < (1 << 29)) {
-          float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + lane);
-          for (int e = k < g.K ? g.K - k : 0; e < 4; ++e) unit[e] = 0.0f;
+        for (int s = 0; s < Cfg::A_SLOTS; ++s) {
+          const int k = t * BK + a_k[s];
+          if (k + 4 > g.K && k < (1 << 29)) {
+            float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + lane);
+            for (int e = k < g.K ? g.K - k : 0; e < 4; ++e) unit[e] = 0.0f;
+          }
         }
+        __builtin_amdgcn_s_waitcnt(kLdsWait);
       }
-      __builtin_amdgcn_s_waitcnt(kLdsWait);
     }
     // A plain workgroup barrier: the waits above already cover this wave's
     // loads of slab t, and the "memory" clobber keeps the compiler from
     // moving LDS accesses across it.  (A full __syncthreads() fence would
     // also wait for the later slabs, which must stay in flight.)
     asm volatile("s_barrier" ::: "memory");
-    const int nk0 = (t + DEPTH) * BK, nst = st == 0 ? STAGES - 1 : st - 1;
-    if (!kSpread) issue(nk0, nst);
+    const int nst = st == 0 ? STAGES - 1 : st - 1;
+    const int nk0 = (t + DEPTH) * BK;
+    const __amdgpu_buffer_rsrc_t qa = rsrc_a(nk0), qb = rsrc_b(nk0);
+    if constexpr (kLoads && !kSpread) issue(qa, qb, nst);
 
     const float* as = As + st * Cfg::A_STAGE;
     const float* bs = Bs + st * Cfg::B_STAGE;
@@ -298,10 +311,12 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
       for (int p = 0; p < 8; ++p) {
         // Load l of the next slab goes before step l * 8 / LOADS of the
         // first sub-slab (whole-slab wave groups only; see the top).
-        if (kSpread && uu == 0) {
+        if constexpr (kLoads && kSpread) {
+          if (uu == 0) {
 #pragma unroll
-          for (int l = 0; l < Cfg::LOADS; ++l)
-            if (p == l * 8 / Cfg::LOADS) issue_one(l, nk0, nst);
+            for (int l = 0; l < Cfg::LOADS; ++l)
+              if (p == l * 8 / Cfg::LOADS) issue_one(l, qa, qb, nst);
+          }
         }
 #pragma unroll
         for (int i = 0; i < TA; ++i)
@@ -311,11 +326,18 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
                 af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
       }
     }
+  };
+
+  int st = 0;  // stage of slab t
+  int t = 0;
+  for (; t + DEPTH < nslab; ++t) {
+    slab(t, st, std::true_type());
     st = (st == STAGES - 1) ? 0 : st + 1;
   }
-  // The loads of the slabs after the last land before the stages are reused
-  // (split-K sum) or the workgroup's LDS is released.
-  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+  for (; t < nslab; ++t) {
+    slab(t, st, std::false_type());
+    st = (st == STAGES - 1) ? 0 : st + 1;
+  }
 
   if constexpr (KS > 1) {
     // Groups 1..KS-1 leave their partial tiles in LDS (lane-contiguous, so
