@@ -280,6 +280,36 @@ VARIANT_SHAPES = [
 ]
 
 
+# (kernel, M, N, K): K a multiple of 4 that ends inside a slab, so in the last
+# slab whole 4-float groups of A lie past k = K; with lda = K + 12 they are
+# A's NaN padding columns, which the kernels must not let reach C.
+K_TAIL_SHAPES = [
+    ("mfma_lds_256x256x32", 4096, 8192, 52),
+    ("mfma_lds_128x128x32", 1536, 8192, 148),
+    ("mfma_lds_64x128x32", 1024, 4096, 452),
+    ("mfma_lds_64x128x32_ks2", 640, 3072, 116),
+    ("mfma_lds_64x64x32", 384, 8192, 452),
+    ("mfma_lds_64x64x32_ks2", 192, 3072, 340),
+    ("mfma_lds_32x64x32_ks2", 192, 8192, 452),
+    ("mfma_lds_32x64x64_ks4", 32, 64, 452),
+]
+
+
+@pytest.mark.parametrize("kernel,M,N,K", K_TAIL_SHAPES, ids=[v[0] for v in K_TAIL_SHAPES])
+def test_every_direct_variant_whole_groups_past_k(kernel, M, N, K):
+    import tiled_fp32_gemm_amd as sg
+    lda = K + 12
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 1800 + K, lda=lda, fill=np.nan)
+    dA, dB = DevMat(A), DevMat(B)
+    dC = DevMat(np.full((M, N), np.nan, np.float32))
+    st, plan = sg.sgemm_plan_query(M, N, K, dA.ptr, lda, dB.ptr, N, dC.ptr, N, 0)
+    assert st == sg.OK and plan.kernel.decode().rsplit("_", 1)[0] == kernel
+    say(f"[gpu] K tail {kernel} M={M} N={N} K={K} lda={lda}")
+    assert run(M, N, K, dA, dB, dC, "auto")
+    Cref, T = oracle.gemm(A[:, :K], B, M=M, N=N, K=K)
+    assert_close(dC.host(), Cref, T, f"K tail {kernel}")
+
+
 @pytest.mark.parametrize("kernel,M,N,K", VARIANT_SHAPES, ids=[v[0] for v in VARIANT_SHAPES])
 @pytest.mark.parametrize("odd_lda", [False, True])
 def test_every_direct_variant(kernel, M, N, K, odd_lda):

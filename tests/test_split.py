@@ -82,6 +82,9 @@ SPLIT_SHAPES = [
     (1, 1024, 65536, 65536, 1024, 1024, 0, "normal", 7),
     (1024, 1, 32768, 32768, 1, 1, 0, "normal", 8),
     (97, 131, 7777, 7779, 133, 131, 3, "uniform", 9),
+    # K a multiple of 4 ending inside a slab: whole A groups of NaN padding
+    # past k = K in the last split's last slab
+    (256, 256, 8180, 8192, 256, 256, 0, "normal", 10),
 ]
 
 
