@@ -67,9 +67,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.txt")
 
 
 def kernel_source_hash() -> str:
-    """Digest of the sources of the product GEMM kernels (device code only;
-    not the transpose, not the ablation ladder's own kernels): the counters
-    recorded under profiles/ stay valid while it is unchanged."""
+    """Digest of the code of the product GEMM kernels (device code only; not
+    the transpose, not the ablation ladder's own kernels; comments and
+    whitespace left out): the counters recorded under profiles/ stay valid
+    while it is unchanged."""
     from tiled_fp32_gemm_amd import build
     h = hashlib.sha256()
     for p in build.sources():
@@ -77,8 +78,11 @@ def kernel_source_hash() -> str:
         if name == "common.hpp" or (name.startswith("kernel_")
                                     and "transpose" not in name
                                     and "ladder" not in name):
+            text = open(p).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(name.encode())
-            h.update(open(p, "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -55,9 +55,9 @@
 // not issued in one burst after the barrier but one at a time between the
 // matrix instructions of its first sub-slab: issued together, the loads of
 // all waves land in LDS at the same moment and hold up the fragment reads
-// (measured on MI355X: 142.3 -> 144.7 TFLOP/s at 4096^3 for the 256 x 256
-// tile, +2% for 128 x 128).  Split-K variants issue them at once: their
-// slabs are short, and a later issue costs them more than the burst.
+// (measured on MI355X: +0.7% at 4096^3 and 8192^3 for the 256 x 256 tile).
+// Split-K variants issue them at once: their slabs are short, and a later
+// issue costs them more than the burst.
 //
 // Split K inside the workgroup (KS > 1, for shapes with too few tiles to fill
 // the chip): KS wave groups compute the same tile over their own sub-slabs
