@@ -30,6 +30,10 @@ workload instead, one JSON line per step.
 workspace of ``sgemm_workspace_bytes``) on the workload, with the plain
 ``sgemm`` of the same shape beside it; the events bracket both of its kernels.
 
+``--op vendor`` times ``sgemm`` and the vendor FP32 GEMM (``torch.matmul``,
+hipBLASLt) side by side on a fixed list of shapes, as context: one JSON line
+per shape, both under the same warm-up and operand rotation.
+
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
 the counter scale factors) and prints its size.  ``--op transpose`` measures
 the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s,
@@ -308,6 +312,89 @@ def bench_ws(args) -> int:
     return 0
 
 
+# Shapes for --op vendor: the five workloads, squares, tall, wide, short-K,
+# long-K and ragged shapes.
+VENDOR_SHAPES = [(256, 256, 256), (512, 512, 512), (1024, 1024, 1024),
+                 (2048, 2048, 2048), (3072, 3072, 3072), (4096, 4096, 4096),
+                 (6144, 6144, 6144), (8192, 8192, 8192), (1000, 1500, 777),
+                 (65536, 128, 256), (16384, 256, 1024), (128, 16384, 1024),
+                 (32768, 512, 512), (4096, 4096, 128), (8192, 8192, 256),
+                 (256, 256, 16384), (512, 512, 8192), (1024, 1024, 8192),
+                 (512, 4096, 4096), (4096, 512, 4096), (3000, 2000, 1111),
+                 (777, 777, 777), (5000, 5000, 300), (12288, 12288, 1024)]
+
+
+def bench_vendor(args) -> int:
+    """sgemm against torch.matmul (the vendor library) on VENDOR_SHAPES."""
+    import numpy as np
+    import torch
+
+    import tiled_fp32_gemm_amd as sg
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sg.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    shapes = VENDOR_SHAPES
+    if args.shapes:
+        shapes = [tuple(int(v) for v in sh.split("x")) for sh in args.shapes.split(",")]
+    for M, N, K in shapes:
+        # operand sets enough to exceed the 256 MiB last-level cache twice
+        nbytes = 4 * (M * K + K * N + M * N)
+        nsets = max(1, min(64, -(-(512 << 20) // nbytes)))
+        sets = [(torch.rand((M, K), device=dev, generator=g) * 2 - 1,
+                 torch.rand((K, N), device=dev, generator=g) * 2 - 1,
+                 torch.empty((M, N), device=dev)) for _ in range(nsets)]
+        ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in sets]
+        cnt = [0, 0]
+
+        def ours():
+            pa, pb, pc = ptrs[cnt[0] % nsets]
+            cnt[0] += 1
+            if sg.sgemm(M, N, K, pa, K, pb, N, pc, N, sh) != sg.OK:
+                raise sg.SgemmError(sg.ERR_LAUNCH, "sgemm")
+
+        def vendor():
+            a, b, c = sets[cnt[1] % nsets]
+            cnt[1] += 1
+            torch.matmul(a, b, out=c)
+
+        need = sg.sgemm_workspace_bytes(M, N, K)
+        ws = torch.empty(max(need // 4, 1), device=dev)
+
+        def ours_ws():
+            pa, pb, pc = ptrs[cnt[0] % nsets]
+            cnt[0] += 1
+            if sg.sgemm_ws(M, N, K, pa, K, pb, N, pc, N, sh, ws.data_ptr(), need) != sg.OK:
+                raise sg.SgemmError(sg.ERR_LAUNCH, "sgemm_ws")
+
+        flops = 2.0 * M * N * K
+        wall, ev, _ = timed_steps(ours, args, stream)
+        wall_v, ev_v, _ = timed_steps(vendor, args, stream)
+        # sgemm_ws is sgemm itself where the planner takes no split
+        wall_w = timed_steps(ours_ws, args, stream)[0] if need > 0 else wall
+        st, plan = sg.sgemm_plan_query(M, N, K, ptrs[0][0], K, ptrs[0][1], N,
+                                       ptrs[0][2], N, 0)
+        print(json.dumps({
+            "metric": "SGEMM TFLOP/s against the vendor library (fp32, 1 GPU)",
+            "M": M, "N": N, "K": K, "operand_sets": nsets,
+            "kernel": plan.kernel.decode(), "steps": args.steps,
+            "sgemm_tflops": round(flops * args.steps / wall / 1e12, 2),
+            "vendor_tflops": round(flops * args.steps / wall_v / 1e12, 2),
+            "sgemm_ws_tflops": round(flops * args.steps / wall_w / 1e12, 2),
+            "ws_splits": sg.sgemm_plan_query_ws(M, N, K, ptrs[0][0], K, ptrs[0][1], N,
+                                                ptrs[0][2], N, need)[1].splits,
+            "sgemm_event_ms_median": round(float(np.median(ev)), 5),
+            "vendor_event_ms_median": round(float(np.median(ev_v)), 5)}),
+            flush=True)
+        del sets, ws
+    return 0
+
+
 def bench_ladder(args) -> int:
     """Every ablation ladder step (sgemm_ladder) on the workload: one JSON
     line per step, in ladder order."""
@@ -391,7 +478,10 @@ def main() -> int:
     ap.add_argument("--event-every", type=int, default=10, metavar="N",
                     help="time every N-th launch of the timed steps with HIP events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--op", default="sgemm", choices=["sgemm", "sgemm_ws", "transpose"])
+    ap.add_argument("--shapes", default=None,
+                    help="--op vendor: comma-separated MxNxK list instead of the built-in one")
+    ap.add_argument("--op", default="sgemm",
+                    choices=["sgemm", "sgemm_ws", "transpose", "vendor"])
     ap.add_argument("--ladder", action="store_true",
                     help="run every ablation ladder step on the workload")
     ap.add_argument("--layout", default="auto",
@@ -423,6 +513,8 @@ def main() -> int:
         return bench_transpose(args)
     if args.op == "sgemm_ws":
         return bench_ws(args)
+    if args.op == "vendor":
+        return bench_vendor(args)
     if args.ladder:
         return bench_ladder(args)
 

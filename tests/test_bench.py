@@ -90,3 +90,14 @@ def test_ladder_lines(capsys):
         check_line(d, 2, 1)
         assert d["config"]["ladder_step"] == step
         assert d["config"]["max_rel_diff_vs_sgemm"] < 1e-5
+
+
+@pytest.mark.gpu
+def test_vendor_lines(capsys):
+    rc, lines = run_main(["--op", "vendor", "--shapes", "256x256x256,96x80x4100",
+                          "--steps", "3", "--warmup", "1"], capsys)
+    assert rc == 0 and len(lines) == 2
+    for d, (M, N, K) in zip(lines, [(256, 256, 256), (96, 80, 4100)]):
+        assert (d["M"], d["N"], d["K"]) == (M, N, K)
+        assert d["sgemm_tflops"] > 0 and d["vendor_tflops"] > 0 and d["sgemm_ws_tflops"] > 0
+    assert lines[1]["ws_splits"] > 1
