@@ -96,6 +96,8 @@ struct DirectCfg {
   static constexpr int A_SLOTS = BM * BK / 4 / NT;
   static constexpr int B_SLOTS = BK * BN / 4 / NT;
   static constexpr int LOADS = A_SLOTS + B_SLOTS;  // vector loads per slab
+  // One wave group with two stages: the chunk-pipelined loop.
+  static constexpr bool CHUNKED = KS == 1 && STAGES == 2;
   static_assert(A_SLOTS * NT * 4 == BM * BK && B_SLOTS * NT * 4 == BK * BN,
                 "slabs must split into whole 64-lane load instructions");
   static_assert(BM % 32 == 0 && BN >= 64 && BN % 64 == 0, "tile shape");
@@ -177,15 +179,20 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   // Unit u = s NT + 64 wave + lane of each load instruction, and the offset
   // of the global 4-float group it takes in slab 0 (kOob when outside the
   // matrix in M or N).
+  // Row and k group of A slot s of this lane.
+  auto a_unit = [&](int s, int ln, int& row, int& c) {
+    const int u = s * NT + 64 * wave + ln;
+    row = (u / (16 * CPR)) * 16 + (u & 15);
+    c = (u >> 4) % CPR;
+  };
   uint32_t a_off[Cfg::A_SLOTS];
-  int a_k[Cfg::A_SLOTS];   // k of the group in its slab; 1 << 30 for rows >= M
 #pragma unroll
   for (int s = 0; s < Cfg::A_SLOTS; ++s) {
-    const int u = s * NT + 64 * wave + lane;
-    const int row = (u / (16 * CPR)) * 16 + (u & 15), c = (u >> 4) % CPR;
-    const bool ok = (m0 + row) < g.M;
-    a_k[s] = ok ? 4 * c : 1 << 30;
-    a_off[s] = ok ? ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u : kOob;
+    int row, c;
+    a_unit(s, lane, row, c);
+    a_off[s] = (m0 + row) < g.M
+                   ? ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u
+                   : kOob;
   }
   uint32_t b_off[Cfg::B_SLOTS];
 #pragma unroll
@@ -231,11 +238,6 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     for (int l = 0; l < Cfg::LOADS; ++l) issue_one(l, qa, qb, st);
   };
 
-  // Spread the loads only where a slab's compute is long (one wave group):
-  // with split K a slab lasts a few hundred cycles per wave, and issuing its
-  // successor's loads any later costs more than the burst does.
-  constexpr bool kSpread = KS == 1;
-
   f32x16 acc[TA][TB];
 #pragma unroll
   for (int i = 0; i < TA; ++i)
@@ -246,97 +248,222 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
 
   const int nslab = (g.K + BK - 1) / BK;
   const bool k_tail = g.K % BK != 0;  // the last slab reaches past k = K
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nslab) issue(rsrc_a(d * BK), rsrc_b(d * BK), d);
 
-  // One slab: wait for its loads, publish it with the barrier, issue slab
-  // t + DEPTH's loads (LOADS, a compile-time flag) and compute.  The slabs
-  // that load are one loop with no branch among their matrix instructions;
-  // the last DEPTH slabs, which load nothing, follow it.
-  auto slab = [&](int t, int st, auto loads) {
-    constexpr bool kLoads = decltype(loads)::value;
-    if constexpr (kLoads) {
-      wait_slabs<Cfg::LOADS, DEPTH>(DEPTH - 1);  // later slabs stay in flight
-    } else {
-      wait_slabs<Cfg::LOADS, DEPTH>(min(DEPTH - 1, nslab - 1 - t));
-      if (k_tail && t == nslab - 1) {
-        // Zero this lane's own A words at k >= K (rows >= M read zeros).
+  // Zeroes this lane's own A words at k >= K of slab t in stage st, once its
+  // loads have landed (rows >= M read zeros already).  Runs once per tile:
+  // the lane's unit is worked out again here rather than kept in registers
+  // through the loop.
+  auto fix_tail = [&](int t, int st) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int s = 0; s < Cfg::A_SLOTS; ++s) {
-          const int k = t * BK + a_k[s];
-          if (k + 4 > g.K && k < (1 << 29)) {
-            float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + lane);
-            for (int e = k < g.K ? g.K - k : 0; e < 4; ++e) unit[e] = 0.0f;
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(kLdsWait);
+    for (int s = 0; s < Cfg::A_SLOTS; ++s) {
+      int row, c;
+      a_unit(s, ln, row, c);
+      const int k = t * BK + 4 * c;
+      if (k + 4 > g.K && m0 + row < g.M) {
+        float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + ln);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k + e >= g.K) unit[e] = 0.0f;
       }
     }
-    // A plain workgroup barrier: the waits above already cover this wave's
-    // loads of slab t, and the "memory" clobber keeps the compiler from
-    // moving LDS accesses across it.  (A full __syncthreads() fence would
-    // also wait for the later slabs, which must stay in flight.)
-    asm volatile("s_barrier" ::: "memory");
-    const int nst = st == 0 ? STAGES - 1 : st - 1;
-    const int nk0 = (t + DEPTH) * BK;
-    const __amdgpu_buffer_rsrc_t qa = rsrc_a(nk0), qb = rsrc_b(nk0);
-    if constexpr (kLoads && !kSpread) issue(qa, qb, nst);
+  };
 
-    const float* as = As + st * Cfg::A_STAGE;
-    const float* bs = Bs + st * Cfg::B_STAGE;
-#pragma unroll
-    for (int uu = 0; uu < SUB_G; ++uu) {
-      const int sub = grp * SUB_G + uu;  // this wave group's sub-slabs
-      f32x4 af[TA][2];
+  if constexpr (Cfg::CHUNKED) {
+    // One wave group, two stages: fragments are read one 8-deep chunk
+    // ahead of the matrix instructions, into two register sets of a chunk
+    // each, and the slab barrier sits before the last chunk's matrix
+    // instructions.  Those run from registers while the next slab's first
+    // chunk is read and the slab after next is loaded, so the barrier and
+    // the first fragment reads of a slab no longer leave the matrix pipe
+    // idle.  The waves of a SIMD arrive at the barrier with a chunk of work
+    // each still to issue.
+    constexpr int NCH = BK / 8;  // chunks per slab (even: BK % 16 == 0)
+    struct Frag {
+      f32x4 a[TA];      // k group 2 lh + (c & 1) of sub-slab c >> 1
+      float b[TB][4];   // 4 k steps
+    };
+    // Chunk c of the slab in stage st: k steps 4 (c & 1) .. 4 (c & 1) + 3 of
+    // sub-slab c >> 1, in the lane layout of the loop below.
+    auto read_chunk = [&](Frag& f, int st, int c) {
+      const float* as = As + st * Cfg::A_STAGE;
+      const float* bs = Bs + st * Cfg::B_STAGE;
+      const int sub = c >> 1, h = c & 1;
 #pragma unroll
       for (int i = 0; i < TA; ++i) {
         const int row = wm0 + 32 * i + li;
         const float* p = as + 4 * ((row >> 4) * (16 * CPR) + (row & 15));
-        af[i][0] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh));
-        af[i][1] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + 1));
+        f.a[i] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + h));
       }
-      float bf[TB][8];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int k = 16 * sub + 8 * lh + p;
+      for (int pp = 0; pp < 4; ++pp) {
+        const int k = 16 * sub + 8 * lh + 4 * h + pp;
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
           const int col = wn0 + 32 * j + li;
           const int q = (col >> 2) ^ (lh ? 8 : 0);
-          bf[j][p] = bs[4 * (k * QB + q) + (col & 3)];
+          f.b[j][pp] = bs[4 * (k * QB + q) + (col & 3)];
         }
       }
+    };
+    // The matrix instructions of a chunk; with LOADS set, load l of the
+    // slab (qa, qb) goes into stage st before k step l * 4 / LOADS.
+    auto mfma_chunk = [&](const Frag& f, auto loads, __amdgpu_buffer_rsrc_t qa,
+                          __amdgpu_buffer_rsrc_t qb, int st) {
+      constexpr bool kLoads = decltype(loads)::value;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        // Load l of the next slab goes before step l * 8 / LOADS of the
-        // first sub-slab (whole-slab wave groups only; see the top).
-        if constexpr (kLoads && kSpread) {
-          if (uu == 0) {
+      for (int pp = 0; pp < 4; ++pp) {
+        if constexpr (kLoads) {
 #pragma unroll
-            for (int l = 0; l < Cfg::LOADS; ++l)
-              if (p == l * 8 / Cfg::LOADS) issue_one(l, qa, qb, nst);
-          }
+          for (int l = 0; l < Cfg::LOADS; ++l)
+            if (pp == l * 4 / Cfg::LOADS) issue_one(l, qa, qb, st);
         }
 #pragma unroll
         for (int i = 0; i < TA; ++i)
 #pragma unroll
           for (int j = 0; j < TB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][pp], f.b[j][pp],
+                                                             acc[i][j], 0, 0, 0);
       }
+    };
+    // Chunks 0 .. NCH-2 of slab t (stage st), each after the read of the
+    // next; the scheduling barriers keep each read ahead of the chunk it
+    // overlaps.
+    Frag fr[2];
+    const __amdgpu_buffer_rsrc_t qz = make_rsrc(g.A, 0u);  // for load-free chunks
+    auto chunks = [&](int st) {
+#pragma unroll
+      for (int c = 0; c + 1 < NCH; ++c) {
+        read_chunk(fr[(c + 1) & 1], st, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_chunk(fr[c & 1], std::false_type(), qz, qz, 0);
+      }
+    };
+    // Slab t (stage st) when a slab t + 1 follows: its chunks, then this
+    // wave's loads of slab t + 1 and its reads of the last chunk are waited
+    // for, the barrier publishes slab t + 1 and frees stage st, the first
+    // chunk of slab t + 1 is read, and the last chunk of slab t computes
+    // while (LOADS set) slab t + 2 is loaded into stage st.
+    auto step = [&](int t, int st, auto loads) {
+      chunks(st);
+      const int nst = st ^ 1;
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      if (k_tail && t + 2 == nslab) fix_tail(t + 1, nst);
+      __builtin_amdgcn_s_waitcnt(kLdsWait);
+      asm volatile("s_barrier" ::: "memory");
+      read_chunk(fr[0], nst, 0);
+      const int k2 = (t + 2) * BK;
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk(fr[1], loads, rsrc_a(k2), rsrc_b(k2), st);
+    };
+    if (nslab > 0) {
+      issue(rsrc_a(0), rsrc_b(0), 0);
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+      if (k_tail && nslab == 1) fix_tail(0, 0);
+      __builtin_amdgcn_s_waitcnt(kLdsWait);
+      asm volatile("s_barrier" ::: "memory");
+      if (nslab > 1) issue(rsrc_a(BK), rsrc_b(BK), 1);
+      read_chunk(fr[0], 0, 0);
+      int t = 0;
+      for (; t + 2 < nslab; ++t) step(t, t & 1, std::true_type());
+      if (t + 1 < nslab) {
+        step(t, t & 1, std::false_type());
+        ++t;
+      }
+      chunks(t & 1);
+      mfma_chunk(fr[1], std::false_type(), qz, qz, 0);
     }
-  };
+  } else {
+    // Spread the loads only where a slab's compute is long (one wave
+    // group): with split K a slab lasts a few hundred cycles per wave, and
+    // issuing its successor's loads any later costs more than the burst
+    // does.
+    constexpr bool kSpread = KS == 1;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (d < nslab) issue(rsrc_a(d * BK), rsrc_b(d * BK), d);
 
-  int st = 0;  // stage of slab t
-  int t = 0;
-  for (; t + DEPTH < nslab; ++t) {
-    slab(t, st, std::true_type());
-    st = (st == STAGES - 1) ? 0 : st + 1;
-  }
-  for (; t < nslab; ++t) {
-    slab(t, st, std::false_type());
-    st = (st == STAGES - 1) ? 0 : st + 1;
+    // One slab: wait for its loads, publish it with the barrier, issue slab
+    // t + DEPTH's loads (LOADS, a compile-time flag) and compute.  The slabs
+    // that load are one loop with no branch among their matrix
+    // instructions; the last DEPTH slabs, which load nothing, follow it.
+    auto slab = [&](int t, int st, auto loads) {
+      constexpr bool kLoads = decltype(loads)::value;
+      if constexpr (kLoads) {
+        wait_slabs<Cfg::LOADS, DEPTH>(DEPTH - 1);  // later slabs stay in flight
+      } else {
+        wait_slabs<Cfg::LOADS, DEPTH>(min(DEPTH - 1, nslab - 1 - t));
+        if (k_tail && t == nslab - 1) {
+          fix_tail(t, st);
+          __builtin_amdgcn_s_waitcnt(kLdsWait);
+        }
+      }
+      // A plain workgroup barrier: the waits above already cover this
+      // wave's loads of slab t, and the "memory" clobber keeps the compiler
+      // from moving LDS accesses across it.  (A full __syncthreads() fence
+      // would also wait for the later slabs, which must stay in flight.)
+      asm volatile("s_barrier" ::: "memory");
+      const int nst = st == 0 ? STAGES - 1 : st - 1;
+      const int nk0 = (t + DEPTH) * BK;
+      const __amdgpu_buffer_rsrc_t qa = rsrc_a(nk0), qb = rsrc_b(nk0);
+      if constexpr (kLoads && !kSpread) issue(qa, qb, nst);
+
+      const float* as = As + st * Cfg::A_STAGE;
+      const float* bs = Bs + st * Cfg::B_STAGE;
+#pragma unroll
+      for (int uu = 0; uu < SUB_G; ++uu) {
+        const int sub = grp * SUB_G + uu;  // this wave group's sub-slabs
+        f32x4 af[TA][2];
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+          const int row = wm0 + 32 * i + li;
+          const float* p = as + 4 * ((row >> 4) * (16 * CPR) + (row & 15));
+          af[i][0] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh));
+          af[i][1] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + 1));
+        }
+        float bf[TB][8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int k = 16 * sub + 8 * lh + p;
+#pragma unroll
+          for (int j = 0; j < TB; ++j) {
+            const int col = wn0 + 32 * j + li;
+            const int q = (col >> 2) ^ (lh ? 8 : 0);
+            bf[j][p] = bs[4 * (k * QB + q) + (col & 3)];
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          // Load l of the next slab goes before step l * 8 / LOADS of the
+          // first sub-slab (whole-slab wave groups only; see above).
+          if constexpr (kLoads && kSpread) {
+            if (uu == 0) {
+#pragma unroll
+              for (int l = 0; l < Cfg::LOADS; ++l)
+                if (p == l * 8 / Cfg::LOADS) issue_one(l, qa, qb, nst);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < TA; ++i)
+#pragma unroll
+            for (int j = 0; j < TB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                  af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
+        }
+      }
+    };
+
+    int st = 0;  // stage of slab t
+    int t = 0;
+    for (; t + DEPTH < nslab; ++t) {
+      slab(t, st, std::true_type());
+      st = (st == STAGES - 1) ? 0 : st + 1;
+    }
+    for (; t < nslab; ++t) {
+      slab(t, st, std::false_type());
+      st = (st == STAGES - 1) ? 0 : st + 1;
+    }
   }
 
   if constexpr (KS > 1) {
@@ -370,15 +497,20 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     }
   }
 
+  // The lane's place in C, worked out again rather than kept in registers
+  // through the loop (the 256 x 256 tile needs every register it may have).
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int li_c = ln & 31, lh_c = ln >> 5;
 #pragma unroll
   for (int i = 0; i < TA; ++i) {
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
-      const int col = n0 + wn0 + 32 * j + li;
+      const int col = n0 + wn0 + 32 * j + li_c;
       const bool col_ok = col < g.N;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lh_c + (r & 3);
         const bool ok = col_ok && row < g.M;
         store1(rc, ok ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob,
                acc[i][j][r]);
