@@ -6,7 +6,8 @@
 // the nearest CDNA4 counterpart of the asynchronous copy the pages mention
 // ("Memory-bank mechanism and accelerated compute", section on alternatives
 // to padding); here it removes the staging registers and the LDS store
-// instructions and keeps STAGES - 1 slabs in flight.
+// instructions, and one slab is in flight while the other is computed (two
+// LDS stages).
 //
 // Alignment and edges.  The load-to-LDS form takes 16 bytes from any
 // 4-byte-aligned address and range-checks each 4-byte word against the
@@ -26,9 +27,10 @@
 //     words with 0 in LDS before the slab's barrier.  This is the pages' rule
 //     that an edge writes 0 for invalid elements ("CUDA in depth (5)",
 //     section on edges).
-// The last STAGES - 1 slabs, which load nothing, are peeled off the main
-// loop, so the loads between the matrix instructions need no branch and
-// every wait count in the loop is the same.
+// The last slab, which loads nothing, and the one before it, whose successor
+// loads nothing, are peeled off the main loop, so the loads between the
+// matrix instructions need no branch and every wait count in the loop is
+// the same.
 //
 // A direct load writes lane l's 16 bytes at base + 16 l, so each layout is
 // chosen as a permutation of 16-byte units that keeps every load instruction
@@ -48,16 +50,22 @@
 //     alternatives to padding, applied at 16-byte granularity so that the
 //     128-bit units stay whole).
 //
-// Pipeline with S stages: up to S - 1 slabs are in flight while slab t is
-// computed; at the top of each step a wave waits until its own loads of slab
-// t have landed, then one barrier makes every wave's loads visible and frees
-// the stage of slab t-1 for slab t + S - 1.  A wave's loads of that slab are
-// not issued in one burst after the barrier but one at a time between the
-// matrix instructions of its first sub-slab: issued together, the loads of
-// all waves land in LDS at the same moment and hold up the fragment reads
-// (measured on MI355X: +0.7% at 4096^3 and 8192^3 for the 256 x 256 tile).
-// Split-K variants issue them at once: their slabs are short, and a later
-// issue costs them more than the burst.
+// Pipeline.  Slabs alternate between the two stages.  A wave reads its MFMA
+// fragments one 8-deep chunk ahead of the matrix instructions that use them,
+// into two register sets of one chunk each (the registers one 16-deep
+// sub-slab would take), and the slab barrier sits before the last chunk's
+// matrix instructions: before it, each wave waits for its own loads of slab
+// t + 1 and its reads of slab t's last chunk; after it, slab t's last chunk
+// computes from registers while slab t + 1's first chunk is read and slab
+// t + 2 is loaded into the stage slab t has left.  The matrix pipe thus has
+// a chunk of every wave's work queued across each barrier and each slab's
+// first fragment reads, which with the fragments read after the barrier
+// left it idle (measured on MI355X: +2% at 4096^3 and 8192^3 for the
+// 256 x 256 tile, +2 to +6% for the smaller tiles).  With one wave group a
+// slab's loads go out one at a time among the last chunk's matrix
+// instructions: issued together, the loads of all waves land in LDS at the
+// same moment and hold up the fragment reads.  With K split inside the
+// workgroup a wave's chunk is short, and the loads go out at once.
 //
 // Split K inside the workgroup (KS > 1, for shapes with too few tiles to fill
 // the chip): KS wave groups compute the same tile over their own sub-slabs
@@ -75,11 +83,10 @@
 
 namespace sg {
 
-template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3,
-          int KS_ = 1>
+template <int BM, int BN, int WM, int WN, int BK_ = 32, int KS_ = 1>
 struct DirectCfg {
-  static constexpr int BK = BK_, STAGES = STAGES_, KS = KS_;
-  static constexpr int DEPTH = STAGES - 1;  // slabs loaded ahead
+  static constexpr int BK = BK_, KS = KS_;
+  static constexpr int STAGES = 2;          // slab buffers in LDS
   static constexpr int SUB = BK / 16;       // 16-deep sub-slabs per slab
   static constexpr int SUB_G = SUB / KS;    // ... per wave group
   static constexpr int CPR = BK / 4;        // 16-byte k groups per A row
@@ -96,13 +103,11 @@ struct DirectCfg {
   static constexpr int A_SLOTS = BM * BK / 4 / NT;
   static constexpr int B_SLOTS = BK * BN / 4 / NT;
   static constexpr int LOADS = A_SLOTS + B_SLOTS;  // vector loads per slab
-  // One wave group with two stages: the chunk-pipelined loop.
-  static constexpr bool CHUNKED = KS == 1 && STAGES == 2;
   static_assert(A_SLOTS * NT * 4 == BM * BK && B_SLOTS * NT * 4 == BK * BN,
                 "slabs must split into whole 64-lane load instructions");
   static_assert(BM % 32 == 0 && BN >= 64 && BN % 64 == 0, "tile shape");
-  static_assert(LOADS * DEPTH < 64, "wait count must fit the 6-bit field");
-  static_assert(BK % 16 == 0 && STAGES >= 2 && DEPTH <= 3, "slabs and stages");
+  static_assert(LOADS < 64, "wait count must fit the 6-bit field");
+  static_assert(BK % 16 == 0, "slabs of whole sub-slabs");
   static_assert(SUB % KS == 0, "each wave group takes whole sub-slabs");
 };
 
@@ -119,31 +124,18 @@ struct VmWait {
 // 0, the other counts at their maxima).
 constexpr int kLdsWait = 0xF | (0x7 << 4) | (0x3 << 14);
 
-// Waits until at most `ahead` slabs of this wave's loads are still in flight.
-template <int LOADS, int DEPTH>
-__device__ __forceinline__ void wait_slabs(int ahead) {
-  if constexpr (DEPTH >= 3) {
-    if (ahead >= 2) { __builtin_amdgcn_s_waitcnt(VmWait<2 * LOADS>::imm); return; }
-  }
-  if constexpr (DEPTH >= 2) {
-    if (ahead >= 1) { __builtin_amdgcn_s_waitcnt(VmWait<LOADS>::imm); return; }
-  }
-  __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
-}
-
-template <int BM, int BN, int WM, int WN, int BK_ = 16, int STAGES_ = 3,
-          int KS_ = 1, bool SPLIT = false>
+template <int BM, int BN, int WM, int WN, int BK_ = 32, int KS_ = 1, bool SPLIT = false>
 __global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN) * KS_)
 sgemm_mfma_direct_kernel(GemmArgs g_in) {
-  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, STAGES_, KS_>;
+  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, KS_>;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
-  constexpr int CPR = Cfg::CPR, STAGES = Cfg::STAGES, DEPTH = Cfg::DEPTH;
+  constexpr int CPR = Cfg::CPR;
   constexpr int KS = Cfg::KS, SUB_G = Cfg::SUB_G;
   constexpr int QB = BN / 4;  // 16-byte units per B row
 
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
-  float* const As = lds;                                // [STAGES][A_STAGE]
-  float* const Bs = lds + Cfg::STAGES * Cfg::A_STAGE;   // [STAGES][B_STAGE]
+  float* const As = lds;                                // [2][A_STAGE]
+  float* const Bs = lds + Cfg::STAGES * Cfg::A_STAGE;   // [2][B_STAGE]
 
   // Split K across workgroups: this workgroup's K range becomes the whole
   // product of a narrower A and a shorter B, its tile goes to the partial
@@ -169,7 +161,10 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave / Cfg::SPATIAL, sw = wave % Cfg::SPATIAL;
+  // Wave group and place in the group (with one group, the wave itself:
+  // said outright, since the compiler cannot know that wave < SPATIAL).
+  const int grp = KS == 1 ? 0 : wave / Cfg::SPATIAL;
+  const int sw = KS == 1 ? wave : wave % Cfg::SPATIAL;
   const int wm0 = (sw / Cfg::WAVES_N) * WM;
   const int wn0 = (sw % Cfg::WAVES_N) * WN;
   const int li = lane & 31, lh = lane >> 5;
@@ -178,8 +173,7 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
 
   // Unit u = s NT + 64 wave + lane of each load instruction, and the offset
   // of the global 4-float group it takes in slab 0 (kOob when outside the
-  // matrix in M or N).
-  // Row and k group of A slot s of this lane.
+  // matrix in M or N).  a_unit gives the row and k group of A slot s.
   auto a_unit = [&](int s, int ln, int& row, int& c) {
     const int u = s * NT + 64 * wave + ln;
     row = (u / (16 * CPR)) * 16 + (u & 15);
@@ -270,200 +264,117 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     }
   };
 
-  if constexpr (Cfg::CHUNKED) {
-    // One wave group, two stages: fragments are read one 8-deep chunk
-    // ahead of the matrix instructions, into two register sets of a chunk
-    // each, and the slab barrier sits before the last chunk's matrix
-    // instructions.  Those run from registers while the next slab's first
-    // chunk is read and the slab after next is loaded, so the barrier and
-    // the first fragment reads of a slab no longer leave the matrix pipe
-    // idle.  The waves of a SIMD arrive at the barrier with a chunk of work
-    // each still to issue.
-    constexpr int NCH = BK / 8;  // chunks per slab (even: BK % 16 == 0)
-    struct Frag {
-      f32x4 a[TA];      // k group 2 lh + (c & 1) of sub-slab c >> 1
-      float b[TB][4];   // 4 k steps
-    };
-    // Chunk c of the slab in stage st: k steps 4 (c & 1) .. 4 (c & 1) + 3 of
-    // sub-slab c >> 1, in the lane layout of the loop below.
-    auto read_chunk = [&](Frag& f, int st, int c) {
-      const float* as = As + st * Cfg::A_STAGE;
-      const float* bs = Bs + st * Cfg::B_STAGE;
-      const int sub = c >> 1, h = c & 1;
+  // Spread the loads only where a slab's compute is long (one wave group):
+  // with split K a slab lasts a few hundred cycles per wave, and issuing its
+  // successor's loads any later costs more than the burst does.
+  constexpr bool kSpread = KS == 1;
+
+  // The chunk pipeline described at the top of the file.
+  constexpr int NCH = 2 * SUB_G;  // chunks per slab of this wave group
+  struct Frag {
+    f32x4 a[TA];      // k group 2 lh + (c & 1) of sub-slab c >> 1
+    float b[TB][4];   // 4 k steps
+  };
+  // Chunk c of the slab in stage st: k steps 4 (c & 1) .. 4 (c & 1) + 3 of
+  // this wave group's sub-slab c >> 1, in the lane layout of the loop
+  // below.
+  auto read_chunk = [&](Frag& f, int st, int c) {
+    const float* as = As + st * Cfg::A_STAGE;
+    const float* bs = Bs + st * Cfg::B_STAGE;
+    const int sub = grp * SUB_G + (c >> 1), h = c & 1;
 #pragma unroll
-      for (int i = 0; i < TA; ++i) {
-        const int row = wm0 + 32 * i + li;
-        const float* p = as + 4 * ((row >> 4) * (16 * CPR) + (row & 15));
-        f.a[i] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + h));
+    for (int i = 0; i < TA; ++i) {
+      const int row = wm0 + 32 * i + li;
+      const float* p = as + 4 * ((row >> 4) * (16 * CPR) + (row & 15));
+      f.a[i] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + h));
+    }
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int k = 16 * sub + 8 * lh + 4 * h + pp;
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        const int col = wn0 + 32 * j + li;
+        const int q = (col >> 2) ^ (lh ? 8 : 0);
+        f.b[j][pp] = bs[4 * (k * QB + q) + (col & 3)];
+      }
+    }
+  };
+  // The matrix instructions of a chunk; with LOADS set, load l of the
+  // slab (qa, qb) goes into stage st before k step l * 4 / LOADS.
+  auto mfma_chunk = [&](const Frag& f, auto loads, __amdgpu_buffer_rsrc_t qa,
+                        __amdgpu_buffer_rsrc_t qb, int st) {
+    constexpr bool kLoads = decltype(loads)::value;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      if constexpr (kLoads) {
+#pragma unroll
+        for (int l = 0; l < Cfg::LOADS; ++l)
+          if (pp == l * 4 / Cfg::LOADS) issue_one(l, qa, qb, st);
       }
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int k = 16 * sub + 8 * lh + 4 * h + pp;
+      for (int i = 0; i < TA; ++i)
 #pragma unroll
-        for (int j = 0; j < TB; ++j) {
-          const int col = wn0 + 32 * j + li;
-          const int q = (col >> 2) ^ (lh ? 8 : 0);
-          f.b[j][pp] = bs[4 * (k * QB + q) + (col & 3)];
-        }
-      }
-    };
-    // The matrix instructions of a chunk; with LOADS set, load l of the
-    // slab (qa, qb) goes into stage st before k step l * 4 / LOADS.
-    auto mfma_chunk = [&](const Frag& f, auto loads, __amdgpu_buffer_rsrc_t qa,
-                          __amdgpu_buffer_rsrc_t qb, int st) {
-      constexpr bool kLoads = decltype(loads)::value;
+        for (int j = 0; j < TB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][pp], f.b[j][pp],
+                                                           acc[i][j], 0, 0, 0);
+    }
+  };
+  // Chunks 0 .. NCH-2 of slab t (stage st), each after the read of the
+  // next; the scheduling barriers keep each read ahead of the chunk it
+  // overlaps.
+  Frag fr[2];
+  const __amdgpu_buffer_rsrc_t qz = make_rsrc(g.A, 0u);  // for load-free chunks
+  auto chunks = [&](int st) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        if constexpr (kLoads) {
-#pragma unroll
-          for (int l = 0; l < Cfg::LOADS; ++l)
-            if (pp == l * 4 / Cfg::LOADS) issue_one(l, qa, qb, st);
-        }
-#pragma unroll
-        for (int i = 0; i < TA; ++i)
-#pragma unroll
-          for (int j = 0; j < TB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][pp], f.b[j][pp],
-                                                             acc[i][j], 0, 0, 0);
-      }
-    };
-    // Chunks 0 .. NCH-2 of slab t (stage st), each after the read of the
-    // next; the scheduling barriers keep each read ahead of the chunk it
-    // overlaps.
-    Frag fr[2];
-    const __amdgpu_buffer_rsrc_t qz = make_rsrc(g.A, 0u);  // for load-free chunks
-    auto chunks = [&](int st) {
-#pragma unroll
-      for (int c = 0; c + 1 < NCH; ++c) {
-        read_chunk(fr[(c + 1) & 1], st, c + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_chunk(fr[c & 1], std::false_type(), qz, qz, 0);
-      }
-    };
-    // Slab t (stage st) when a slab t + 1 follows: its chunks, then this
-    // wave's loads of slab t + 1 and its reads of the last chunk are waited
-    // for, the barrier publishes slab t + 1 and frees stage st, the first
-    // chunk of slab t + 1 is read, and the last chunk of slab t computes
-    // while (LOADS set) slab t + 2 is loaded into stage st.
-    auto step = [&](int t, int st, auto loads) {
-      chunks(st);
-      const int nst = st ^ 1;
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
-      if (k_tail && t + 2 == nslab) fix_tail(t + 1, nst);
-      __builtin_amdgcn_s_waitcnt(kLdsWait);
-      asm volatile("s_barrier" ::: "memory");
+    for (int c = 0; c + 1 < NCH; ++c) {
+      read_chunk(fr[(c + 1) & 1], st, c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk(fr[c & 1], std::false_type(), qz, qz, 0);
+    }
+  };
+  // Slab t (stage st) when a slab t + 1 follows: its chunks, then this
+  // wave's loads of slab t + 1 and its reads of the last chunk are waited
+  // for, the barrier publishes slab t + 1 and frees stage st, the first
+  // chunk of slab t + 1 is read, and the last chunk of slab t computes
+  // while (LOADS set) slab t + 2 is loaded into stage st.
+  auto step = [&](int t, int st, auto loads) {
+    constexpr bool kLoads = decltype(loads)::value;
+    chunks(st);
+    const int nst = st ^ 1;
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    if (k_tail && t + 2 == nslab) fix_tail(t + 1, nst);
+    __builtin_amdgcn_s_waitcnt(kLdsWait);
+    asm volatile("s_barrier" ::: "memory");
+    const int k2 = (t + 2) * BK;
+    if constexpr (kSpread) {
       read_chunk(fr[0], nst, 0);
-      const int k2 = (t + 2) * BK;
       __builtin_amdgcn_sched_barrier(0);
       mfma_chunk(fr[1], loads, rsrc_a(k2), rsrc_b(k2), st);
-    };
-    if (nslab > 0) {
-      issue(rsrc_a(0), rsrc_b(0), 0);
-      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
-      if (k_tail && nslab == 1) fix_tail(0, 0);
-      __builtin_amdgcn_s_waitcnt(kLdsWait);
-      asm volatile("s_barrier" ::: "memory");
-      if (nslab > 1) issue(rsrc_a(BK), rsrc_b(BK), 1);
-      read_chunk(fr[0], 0, 0);
-      int t = 0;
-      for (; t + 2 < nslab; ++t) step(t, t & 1, std::true_type());
-      if (t + 1 < nslab) {
-        step(t, t & 1, std::false_type());
-        ++t;
-      }
-      chunks(t & 1);
-      mfma_chunk(fr[1], std::false_type(), qz, qz, 0);
+    } else {
+      // With K split inside the workgroup a wave's chunk is short: its
+      // loads go out at once.
+      if constexpr (kLoads) issue(rsrc_a(k2), rsrc_b(k2), st);
+      read_chunk(fr[0], nst, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk(fr[1], std::false_type(), qz, qz, st);
     }
-  } else {
-    // Spread the loads only where a slab's compute is long (one wave
-    // group): with split K a slab lasts a few hundred cycles per wave, and
-    // issuing its successor's loads any later costs more than the burst
-    // does.
-    constexpr bool kSpread = KS == 1;
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-      if (d < nslab) issue(rsrc_a(d * BK), rsrc_b(d * BK), d);
-
-    // One slab: wait for its loads, publish it with the barrier, issue slab
-    // t + DEPTH's loads (LOADS, a compile-time flag) and compute.  The slabs
-    // that load are one loop with no branch among their matrix
-    // instructions; the last DEPTH slabs, which load nothing, follow it.
-    auto slab = [&](int t, int st, auto loads) {
-      constexpr bool kLoads = decltype(loads)::value;
-      if constexpr (kLoads) {
-        wait_slabs<Cfg::LOADS, DEPTH>(DEPTH - 1);  // later slabs stay in flight
-      } else {
-        wait_slabs<Cfg::LOADS, DEPTH>(min(DEPTH - 1, nslab - 1 - t));
-        if (k_tail && t == nslab - 1) {
-          fix_tail(t, st);
-          __builtin_amdgcn_s_waitcnt(kLdsWait);
-        }
-      }
-      // A plain workgroup barrier: the waits above already cover this
-      // wave's loads of slab t, and the "memory" clobber keeps the compiler
-      // from moving LDS accesses across it.  (A full __syncthreads() fence
-      // would also wait for the later slabs, which must stay in flight.)
-      asm volatile("s_barrier" ::: "memory");
-      const int nst = st == 0 ? STAGES - 1 : st - 1;
-      const int nk0 = (t + DEPTH) * BK;
-      const __amdgpu_buffer_rsrc_t qa = rsrc_a(nk0), qb = rsrc_b(nk0);
-      if constexpr (kLoads && !kSpread) issue(qa, qb, nst);
-
-      const float* as = As + st * Cfg::A_STAGE;
-      const float* bs = Bs + st * Cfg::B_STAGE;
-#pragma unroll
-      for (int uu = 0; uu < SUB_G; ++uu) {
-        const int sub = grp * SUB_G + uu;  // this wave group's sub-slabs
-        f32x4 af[TA][2];
-#pragma unroll
-        for (int i = 0; i < TA; ++i) {
-          const int row = wm0 + 32 * i + li;
-          const float* p = as + 4 * ((row >> 4) * (16 * CPR) + (row & 15));
-          af[i][0] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh));
-          af[i][1] = *reinterpret_cast<const f32x4*>(p + 4 * 16 * (4 * sub + 2 * lh + 1));
-        }
-        float bf[TB][8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int k = 16 * sub + 8 * lh + p;
-#pragma unroll
-          for (int j = 0; j < TB; ++j) {
-            const int col = wn0 + 32 * j + li;
-            const int q = (col >> 2) ^ (lh ? 8 : 0);
-            bf[j][p] = bs[4 * (k * QB + q) + (col & 3)];
-          }
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          // Load l of the next slab goes before step l * 8 / LOADS of the
-          // first sub-slab (whole-slab wave groups only; see above).
-          if constexpr (kLoads && kSpread) {
-            if (uu == 0) {
-#pragma unroll
-              for (int l = 0; l < Cfg::LOADS; ++l)
-                if (p == l * 8 / Cfg::LOADS) issue_one(l, qa, qb, nst);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < TA; ++i)
-#pragma unroll
-            for (int j = 0; j < TB; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                  af[i][p >> 2][p & 3], bf[j][p], acc[i][j], 0, 0, 0);
-        }
-      }
-    };
-
-    int st = 0;  // stage of slab t
+  };
+  if (nslab > 0) {
+    issue(rsrc_a(0), rsrc_b(0), 0);
+    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    if (k_tail && nslab == 1) fix_tail(0, 0);
+    __builtin_amdgcn_s_waitcnt(kLdsWait);
+    asm volatile("s_barrier" ::: "memory");
+    if (nslab > 1) issue(rsrc_a(BK), rsrc_b(BK), 1);
+    read_chunk(fr[0], 0, 0);
     int t = 0;
-    for (; t + DEPTH < nslab; ++t) {
-      slab(t, st, std::true_type());
-      st = (st == STAGES - 1) ? 0 : st + 1;
+    for (; t + 2 < nslab; ++t) step(t, t & 1, std::true_type());
+    if (t + 1 < nslab) {
+      step(t, t & 1, std::false_type());
+      ++t;
     }
-    for (; t < nslab; ++t) {
-      slab(t, st, std::false_type());
-      st = (st == STAGES - 1) ? 0 : st + 1;
-    }
+    chunks(t & 1);
+    mfma_chunk(fr[1], std::false_type(), qz, qz, 0);
   }
 
   if constexpr (KS > 1) {

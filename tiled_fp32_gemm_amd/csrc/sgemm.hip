@@ -107,12 +107,12 @@ Variant reg_variant(const char* name) {
 
 // The LDS-direct kernel takes rows of any 4-byte alignment, so one kernel
 // serves every load form.
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int KS>
+template <int BM, int BN, int WM, int WN, int BK, int KS>
 Variant direct_variant(const char* name) {
-  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, STAGES, KS>;
-  const KernelFn f = sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES, KS>;
+  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, KS>;
+  const KernelFn f = sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, KS>;
   return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, f, f, f, f,
-          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, STAGES, KS, true>};
+          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, KS, true>};
 }
 
 // Matrix-core configurations, large to small tiles, with the planner's two
@@ -142,14 +142,14 @@ const Candidate* mfma_candidates(bool direct, int& n) {
   // barriers per flop against 16-deep slabs in three stages.  "ks" names the
   // number of wave groups that split each slab.
   static const Candidate lds[8] = {
-      {direct_variant<256, 256, 64, 64, 32, 2, 1>("mfma_lds_256x256x32"), 0.929, 1},
-      {direct_variant<128, 128, 64, 32, 32, 2, 1>("mfma_lds_128x128x32"), 0.868, 2},
-      {direct_variant<64, 128, 32, 64, 32, 2, 1>("mfma_lds_64x128x32"), 0.901, 3},
-      {direct_variant<64, 128, 32, 64, 32, 2, 2>("mfma_lds_64x128x32_ks2"), 0.805, 3},
-      {direct_variant<64, 64, 32, 32, 32, 2, 1>("mfma_lds_64x64x32"), 0.837, 5},
-      {direct_variant<64, 64, 32, 32, 32, 2, 2>("mfma_lds_64x64x32_ks2"), 0.830, 4},
-      {direct_variant<32, 64, 32, 32, 32, 2, 2>("mfma_lds_32x64x32_ks2"), 0.799, 6},
-      {direct_variant<32, 64, 32, 32, 64, 2, 4>("mfma_lds_32x64x64_ks4"), 0.807, 3}};
+      {direct_variant<256, 256, 64, 64, 32, 1>("mfma_lds_256x256x32"), 0.929, 1},
+      {direct_variant<128, 128, 64, 32, 32, 1>("mfma_lds_128x128x32"), 0.868, 2},
+      {direct_variant<64, 128, 32, 64, 32, 1>("mfma_lds_64x128x32"), 0.901, 3},
+      {direct_variant<64, 128, 32, 64, 32, 2>("mfma_lds_64x128x32_ks2"), 0.805, 3},
+      {direct_variant<64, 64, 32, 32, 32, 1>("mfma_lds_64x64x32"), 0.837, 5},
+      {direct_variant<64, 64, 32, 32, 32, 2>("mfma_lds_64x64x32_ks2"), 0.830, 4},
+      {direct_variant<32, 64, 32, 32, 32, 2>("mfma_lds_32x64x32_ks2"), 0.799, 6},
+      {direct_variant<32, 64, 32, 32, 64, 4>("mfma_lds_32x64x64_ks4"), 0.807, 3}};
   n = direct ? 8 : 3;
   return direct ? lds : reg;
 }
