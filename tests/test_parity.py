@@ -271,7 +271,7 @@ def test_largest_operand(K):
 VARIANT_SHAPES = [
     ("mfma_lds_256x256x32", 2048, 8192, 450),
     ("mfma_lds_128x128x32", 4096, 4096, 22),
-    ("mfma_lds_64x128x32", 2048, 2048, 45),
+    ("mfma_lds_64x128x32", 3072, 2048, 45),
     ("mfma_lds_64x128x32_ks2", 640, 3072, 42),
     ("mfma_lds_64x64x32", 1536, 3072, 47),
     ("mfma_lds_64x64x32_ks2", 3072, 192, 53),

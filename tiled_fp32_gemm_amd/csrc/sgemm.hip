@@ -119,8 +119,10 @@ Variant direct_variant(const char* name) {
 // inputs for each:
 //   eff  the fraction of a CU's FP32 matrix peak the variant sustains with
 //        its pipes busy (fitted, with the constants below, to MI355X timings
-//        of every variant on 196 shapes from 96 to 65536 per side, chosen
-//        within 0.4% of the fastest variant on average);
+//        of every variant on 196 shapes from 96 to 65536 per side; after the
+//        kernels' chunk pipeline the 128 x 128 value alone was raised, which
+//        brings the picks within 0.6% of the fastest variant on average over
+//        170 re-timed shapes);
 //   occ  the workgroups a CU holds at once, from the kernel's LDS bytes and
 //        its registers per lane (512 per SIMD lane, at most 8 waves per
 //        SIMD) as compiled for gfx950.
@@ -143,7 +145,7 @@ const Candidate* mfma_candidates(bool direct, int& n) {
   // number of wave groups that split each slab.
   static const Candidate lds[8] = {
       {direct_variant<256, 256, 64, 64, 32, 1>("mfma_lds_256x256x32"), 0.929, 1},
-      {direct_variant<128, 128, 64, 32, 32, 1>("mfma_lds_128x128x32"), 0.868, 2},
+      {direct_variant<128, 128, 64, 32, 32, 1>("mfma_lds_128x128x32"), 0.895, 2},
       {direct_variant<64, 128, 32, 64, 32, 1>("mfma_lds_64x128x32"), 0.901, 3},
       {direct_variant<64, 128, 32, 64, 32, 2>("mfma_lds_64x128x32_ks2"), 0.805, 3},
       {direct_variant<64, 64, 32, 32, 32, 1>("mfma_lds_64x64x32"), 0.837, 5},
