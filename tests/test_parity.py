@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 ALGOS = ["auto", "mfma_direct", "mfma", "fma", "simple"]
 
 # The five workloads: (name, M, N, K, lda, ldb, ldc, distribution, seed).
-CONFIGS = {
+WORKLOAD_SHAPES = {
     "256cube": (256, 256, 256, 256, 256, 256, "uniform", 1),
     "4096cube": (4096, 4096, 4096, 4096, 4096, 4096, "uniform", 2),
     "ragged": (1000, 1500, 777, 777, 1500, 1500, "uniform", 3),
@@ -30,7 +30,7 @@ _inputs: dict = {}
 
 def config_inputs(name):
     if name not in _inputs:
-        M, N, K, lda, ldb, ldc, dist, seed = CONFIGS[name]
+        M, N, K, lda, ldb, ldc, dist, seed = WORKLOAD_SHAPES[name]
         say(f"[inputs] {name}: M={M} N={N} K={K} {dist} seed={seed}")
         A, B = seedgen.gemm_inputs(M, N, K, dist, seed, lda=lda, ldb=ldb)
         _inputs[name] = (A, B, DevMat(A), DevMat(B))
@@ -46,7 +46,7 @@ def _cleanup():
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("name", ["256cube", "ragged", "skinny"])
 def test_config_full(name, algo):
-    M, N, K, lda, ldb, ldc, dist, seed = CONFIGS[name]
+    M, N, K, lda, ldb, ldc, dist, seed = WORKLOAD_SHAPES[name]
     A, B, dA, dB = config_inputs(name)
     dC = DevMat(np.full((M, ldc), np.nan, np.float32))
     say(f"[gpu] {name} algo={algo}")
@@ -71,7 +71,7 @@ def sample_indices(n: int, count: int, tile: int, seed: int) -> np.ndarray:
 def test_config_sampled(name, algo):
     """Full-size shapes: the GPU computes all of C; the oracle computes every
     element of sampled rows and of sampled columns."""
-    M, N, K, lda, ldb, ldc, dist, seed = CONFIGS[name]
+    M, N, K, lda, ldb, ldc, dist, seed = WORKLOAD_SHAPES[name]
     A, B, dA, dB = config_inputs(name)
     dC = DevMat(np.full((M, ldc), np.nan, np.float32))
     say(f"[gpu] {name} algo={algo}")
