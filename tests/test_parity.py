@@ -310,6 +310,57 @@ def test_every_direct_variant_whole_groups_past_k(kernel, M, N, K):
     assert_close(dC.host(), Cref, T, f"K tail {kernel}")
 
 
+# (kernel, M, N, K): one, two and three slabs, the last one partial, so that
+# each variant runs its single-slab path, the peeled step with no loads, and
+# one step with loads before it (integer data: every order gives the same
+# bits).
+SHORT_K_SHAPES = [
+    ("mfma_lds_128x128x32", 637, 4101, 9),
+    ("mfma_lds_128x128x32", 381, 8197, 51),
+    ("mfma_lds_128x128x32", 381, 8197, 83),
+    ("mfma_lds_64x128x32", 637, 8197, 9),
+    ("mfma_lds_64x128x32", 637, 8197, 51),
+    ("mfma_lds_64x128x32", 637, 8197, 83),
+    ("mfma_lds_64x128x32_ks2", 1533, 645, 9),
+    ("mfma_lds_64x128x32_ks2", 189, 8197, 51),
+    ("mfma_lds_64x128x32_ks2", 189, 8197, 83),
+    ("mfma_lds_64x64x32", 4093, 389, 9),
+    ("mfma_lds_64x64x32", 4093, 389, 51),
+    ("mfma_lds_64x64x32", 4093, 389, 83),
+    ("mfma_lds_64x64x32_ks2", 32, 37, 9),
+    ("mfma_lds_64x64x32_ks2", 3069, 133, 51),
+    ("mfma_lds_64x64x32_ks2", 3069, 133, 83),
+    ("mfma_lds_32x64x32_ks2", 32, 1029, 9),
+    ("mfma_lds_32x64x32_ks2", 6141, 133, 51),
+    ("mfma_lds_32x64x32_ks2", 93, 8197, 83),
+    ("mfma_lds_32x64x64_ks4", 32, 37, 99),
+    ("mfma_lds_32x64x64_ks4", 32, 37, 163),
+]
+
+
+@pytest.mark.parametrize("kernel,M,N,K", SHORT_K_SHAPES,
+                         ids=[f"{v[0]}-K{v[3]}" for v in SHORT_K_SHAPES])
+def test_every_direct_variant_one_to_three_slabs(kernel, M, N, K):
+    import tiled_fp32_gemm_amd as sg
+    lda, ldc = K + 1, N + 2
+    A = np.full((M, lda), np.nan, np.float32)
+    A[:, :K] = seedgen.integer_matrix(M, K, -8, 8, 2100 + K)
+    B = seedgen.integer_matrix(K, N, -8, 8, 2100 + K, start=M * K)
+    dA, dB = DevMat(A), DevMat(B)
+    dC = DevMat(np.full((M, ldc), np.nan, np.float32))
+    st, plan = sg.sgemm_plan_query(M, N, K, dA.ptr, lda, dB.ptr, N, dC.ptr, ldc, 0)
+    assert st == sg.OK and plan.kernel.decode().rsplit("_", 1)[0] == kernel
+    say(f"[gpu] short K {kernel} M={M} N={N} K={K}")
+    st = sg.sgemm(M, N, K, dA.ptr, lda, dB.ptr, N, dC.ptr, ldc,
+                  torch.cuda.current_stream().cuda_stream)
+    assert st == sg.OK
+    torch.cuda.synchronize()
+    C = dC.host()
+    Cref, _ = oracle.gemm(A[:, :K], B, M=M, N=N, K=K, with_t=False)
+    assert np.array_equal(C[:, :N], Cref.astype(np.float32))
+    assert np.all(np.isnan(C[:, N:])), "C padding written"
+
+
 @pytest.mark.parametrize("kernel,M,N,K", VARIANT_SHAPES, ids=[v[0] for v in VARIANT_SHAPES])
 @pytest.mark.parametrize("odd_lda", [False, True])
 def test_every_direct_variant(kernel, M, N, K, odd_lda):
