@@ -355,8 +355,9 @@ def bench_vendor(args) -> int:
         def ours():
             pa, pb, pc = ptrs[cnt[0] % nsets]
             cnt[0] += 1
-            if sg.sgemm(M, N, K, pa, K, pb, N, pc, N, sh) != sg.OK:
-                raise sg.SgemmError(sg.ERR_LAUNCH, "sgemm")
+            st = sg.sgemm(M, N, K, pa, K, pb, N, pc, N, sh)
+            if st != sg.OK:
+                raise sg.SgemmError(st, "sgemm")
 
         def vendor():
             a, b, c = sets[cnt[1] % nsets]
@@ -369,8 +370,9 @@ def bench_vendor(args) -> int:
         def ours_ws():
             pa, pb, pc = ptrs[cnt[0] % nsets]
             cnt[0] += 1
-            if sg.sgemm_ws(M, N, K, pa, K, pb, N, pc, N, sh, ws.data_ptr(), need) != sg.OK:
-                raise sg.SgemmError(sg.ERR_LAUNCH, "sgemm_ws")
+            st = sg.sgemm_ws(M, N, K, pa, K, pb, N, pc, N, sh, ws.data_ptr(), need)
+            if st != sg.OK:
+                raise sg.SgemmError(st, "sgemm_ws")
 
         flops = 2.0 * M * N * K
         wall, ev, _ = timed_steps(ours, args, stream)
@@ -415,8 +417,9 @@ def bench_ladder(args) -> int:
     ref = torch.empty_like(tC)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    if sg.sgemm(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N, ref.data_ptr(), N, sh) != sg.OK:
-        raise sg.SgemmError(sg.ERR_LAUNCH, "sgemm")
+    st = sg.sgemm(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N, ref.data_ptr(), N, sh)
+    if st != sg.OK:
+        raise sg.SgemmError(st, "sgemm")
     flops = 2.0 * M * N * K
     for step, name in enumerate(sg.ladder_steps()):
         def run():
