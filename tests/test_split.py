@@ -228,3 +228,25 @@ def test_split_power_of_two_scaling_is_exact():
         res.append(dC.host())
     assert np.array_equal(res[1], 2.0 * res[0])
     assert np.array_equal(res[2], 0.25 * res[0])
+
+
+def test_matmul_with_a_workspace_tensor():
+    """The tensor convenience with a workspace: K split across workgroups on
+    an under-filled long-K shape, within tolerance of the oracle; a bad
+    workspace or algo is refused before any launch."""
+    import tiled_fp32_gemm_amd as sg
+    M, N, K = 200, 300, 10001
+    A, B = seedgen.gemm_inputs(M, N, K, "normal", 95)
+    tA, tB = torch.from_numpy(A).to("cuda:0"), torch.from_numpy(B).to("cuda:0")
+    need = sg.sgemm_workspace_bytes(M, N, K)
+    assert need > 0
+    ws = torch.empty(need // 4, device="cuda:0")
+    say(f"[gpu] matmul with workspace {M}x{N}x{K} ({need} bytes)")
+    out = sg.matmul(tA, tB, workspace=ws)
+    torch.cuda.synchronize()
+    Cref, T = oracle.gemm(A, B)
+    assert_close(out.cpu().numpy(), Cref, T, "matmul workspace")
+    with pytest.raises(ValueError):
+        sg.matmul(tA, tB, algo="fma", workspace=ws)
+    with pytest.raises(ValueError):
+        sg.matmul(tA, tB, workspace=ws.cpu())

@@ -235,12 +235,16 @@ def _args(A, B, out):
     return M, N, K, _ld(A, "A"), _ld(B, "B"), _ld(out, "out")
 
 
-def matmul(A, B, out=None, algo: str | int = "auto", stream=None):
+def matmul(A, B, out=None, algo: str | int = "auto", stream=None, workspace=None):
     """``out = A @ B`` for float32 GPU tensors (row-major, any row stride).
 
     The product runs in the library's kernels on ``stream`` (a
-    ``torch.cuda.Stream``; default: the current stream).  Raises
-    ``ValueError`` on bad tensors and ``SgemmError`` on a library error.
+    ``torch.cuda.Stream``; default: the current stream).  With
+    ``workspace`` (a GPU tensor on the same device, contiguous; its bytes
+    are the room given, see ``sgemm_workspace_bytes``) the call goes through
+    ``sgemm_ws`` and may split K across workgroups; ``algo`` must then be
+    "auto".  Raises ``ValueError`` on bad tensors and ``SgemmError`` on a
+    library error.
     """
     import torch
     if out is None:
@@ -249,6 +253,18 @@ def matmul(A, B, out=None, algo: str | int = "auto", stream=None):
     M, N, K, lda, ldb, ldc = _args(A, B, out)
     code = ALGOS[algo] if isinstance(algo, str) else int(algo)
     s = torch.cuda.current_stream(A.device) if stream is None else stream
+    if workspace is not None:
+        if code != ALGOS["auto"]:
+            raise ValueError("a workspace is used by the auto plan only")
+        if not workspace.is_cuda or workspace.device != A.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on A's device")
+        nbytes = workspace.numel() * workspace.element_size()
+        with torch.cuda.device(A.device):
+            st = sgemm_ws(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                          out.data_ptr(), ldc, s.cuda_stream, workspace.data_ptr(), nbytes)
+        if st != OK:
+            raise SgemmError(st, "sgemm_ws")
+        return out
     with torch.cuda.device(A.device):
         st = sgemm_ex(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
                       out.data_ptr(), ldc, s.cuda_stream, code)
