@@ -60,8 +60,8 @@
 // t + 2 is loaded into the stage slab t has left.  The matrix pipe thus has
 // a chunk of every wave's work queued across each barrier and each slab's
 // first fragment reads, which with the fragments read after the barrier
-// left it idle (measured on MI355X: +2% at 4096^3 and 8192^3 for the
-// 256 x 256 tile, +2 to +6% for the smaller tiles).  With one wave group a
+// left it idle (measured on MI355X: +1 to +2% at 4096^3 and 8192^3 for the
+// 256 x 256 tile, +2 to +6% for the smaller tiles on mid-size shapes).  With one wave group a
 // slab's loads go out one at a time among the last chunk's matrix
 // instructions: issued together, the loads of all waves land in LDS at the
 // same moment and hold up the fragment reads.  With K split inside the
