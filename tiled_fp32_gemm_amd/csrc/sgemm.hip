@@ -222,6 +222,10 @@ const Candidate& choose_mfma(int64_t M, int64_t N, int64_t K, bool direct) {
 constexpr double kReduceFixed = 3.0e-6;  // s
 constexpr double kReduceBW = 5.0e12;     // B/s, a device copy's rate
 constexpr double kSplitMargin = 0.97;    // split only when clearly faster
+// The model over-states the partial pass, whose workgroups see short K and
+// fill the CUs evenly; scaled by this (one value, chosen on timings of every
+// plan on 64 under-filled shapes and checked on each half of them).
+constexpr double kSplitPartial = 0.95;
 
 struct Choice {
   const Candidate* c;
@@ -246,7 +250,7 @@ Choice choose_direct(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
       if (se < 2) continue;
       const int64_t bytes = se * M * N * 4;
       if (bytes > ws_bytes || bytes >= kMaxOperandBytes) continue;
-      const double t = estimate_grid(c, tiles * se, ks) + kReduceFixed +
+      const double t = kSplitPartial * estimate_grid(c, tiles * se, ks) + kReduceFixed +
                        (double)(se + 1) * M * N * 4.0 / kReduceBW;
       if (split.splits == 1 || t < t_best) {
         split = {&c, (int)se, (int)ks};
