@@ -6,12 +6,16 @@ row-major, A and B uniform on [-1, 1) from seed 2) with A, B and C resident in
 HBM.  For the skinny workload, whose operands would fit in the 256 MiB
 last-level cache, the steps rotate over three operand sets (``--buffers``).
 
-W untimed steps (by default as many as take 0.3 s, at least 20: an idle GPU
-needs tens of milliseconds of work to reach its full clock), then K timed
-steps bracketed by device synchronisation.  Every --event-every-th launch of
-the timed steps is also bracketed by a pair of HIP events on the stream it is
-enqueued on (each pair adds a few microseconds between kernels, so they are
-not put around every launch).  Prints one JSON line.
+Untimed launches first: a clock ramp of at least --warmup-seconds (0.3 s)
+of launches, since an idle GPU needs tens of milliseconds of work to reach
+its full clock, then the W counted warm-up steps (--warmup, default 10).
+Then K timed steps bracketed by device synchronisation.  Every
+--event-every-th launch of the timed steps, and more often when K is small
+(at least min(10, K) of them), is also bracketed by a pair of HIP events on
+the stream it is enqueued on (each pair adds a few microseconds between
+kernels, so they are not put around every launch).  Right after the timed
+steps a fixed-work FP32 matrix-core kernel (libsgemm_probe.so) reads the
+clock the matrix pipes run at.  Prints one JSON line.
 
   value            2MNK * K / wall time of the K steps, TFLOP/s
   roofline         the GEMM kernel against the FP32 matrix peak (157.3
@@ -20,8 +24,15 @@ not put around every launch).  Prints one JSON line.
                    WRITE_SIZE counters recorded under profiles/, each scaled
                    by the factor a plain copy of known size gives, or null
                    when the kernel sources changed since they were taken
+  config.clock     the probe's rate and the clock it implies (its matrix
+                   instructions hold each SIMD's pipe a known number of
+                   cycles), and the shader clock read from its counters
   cpu_baseline     the CPU oracle on a bounded row sample of the same product,
-                   repeated for about --cpu-seconds
+                   repeated for about --cpu-seconds; the same leg first
+                   checks the GPU's C on those rows against the oracle
+                   (max |C - Cref| / (|A|.|B|) <= 1e-5, else exit status 3)
+                   and times the whole 256cube and ragged products on one
+                   core
 
 ``--ladder`` runs every step of the ablation ladder (``sgemm_ladder``) on the
 workload instead, one JSON line per step.
@@ -105,24 +116,112 @@ def read_traffic(kernel: str, workload: str, src_hash: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(A, B, M, N, K, rows: int, seconds: float) -> dict:
-    """The oracle on rows 0..rows-1 of the product, repeated until `seconds`
-    of CPU time have passed (at least once, at most 50 times)."""
+TOLERANCE = 1e-5   # |C - Cref| <= TOLERANCE * (|A|.|B|), elementwise
+
+
+def cpu_baseline(A, B, M, N, K, rows: int, seconds: float, gpu_rows) -> tuple:
+    """The CPU leg: the oracle on rows 0..rows-1 of the product.  Its first,
+    untimed, run (with the magnitude sums |A|.|B|) is the reference that
+    gpu_rows(rows) -- the GPU's C, rows 0..rows-1 -- is checked against; then
+    the C-only run is repeated until `seconds` of CPU time have passed (at
+    least once, at most 50 times) for the baseline figure.  Also times the
+    whole 256cube and ragged products on one core.  Returns (baseline dict,
+    check dict)."""
+    import numpy as np
+
     import oracle
+    import seedgen
     rows = min(rows, M)
     sub = A[:rows]
-    oracle.gemm(sub[:8], B, with_t=False)           # load + warm the library
+    Cref, T = oracle.gemm(sub, B, with_t=True)
+    C = gpu_rows(rows).astype(np.float64)
+    err = np.abs(C - Cref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        norm = np.where(T > 0, err / T, np.where(err > 0, np.inf, 0.0))
+    worst = float(norm.max()) if norm.size else 0.0
+    ok = bool(np.all(np.isfinite(C)) and worst <= TOLERANCE)
+    check = {"rows": f"0..{rows - 1}", "elements": int(C.size),
+             "max_err_norm": worst, "tolerance": TOLERANCE, "ok": ok}
+    del Cref, T, C, err, norm
     reps, total = 0, 0.0
     while reps < 50 and (reps == 0 or total < seconds):
         t0 = time.perf_counter()
         oracle.gemm(sub, B, with_t=False)
         total += time.perf_counter() - t0
         reps += 1
-    return {"value": round(2.0 * rows * N * K * reps / total / 1e12, 6),
+    one_core = {}
+    for name in ("256cube", "ragged"):
+        m, n, k, dist, seed = WORKLOADS[name]
+        a, b = seedgen.gemm_inputs(m, n, k, dist, seed)
+        t0 = time.perf_counter()
+        oracle.gemm(a, b, with_t=False, threads=1)
+        dt = time.perf_counter() - t0
+        one_core[name] = {"seconds": round(dt, 4),
+                          "gflops": round(2.0 * m * n * k / dt / 1e9, 3)}
+    base = {"value": round(2.0 * rows * N * K * reps / total / 1e12, 6),
             "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product "
                       f"(C only, fp64 accumulation), {reps} run(s) in "
-                      f"{total:.2f} s"}
+                      f"{total:.2f} s",
+            "one_core": one_core}
+    return base, check
+
+
+def clock_probe(stream, repeats: int = 5, iters: int = 2048) -> dict:
+    """Runs the matrix-core clock probe `repeats` times between HIP events.
+    Each SIMD's matrix pipe is busy for iters * MFMA_PER_ITER * (WAVES / 4) *
+    MFMA_CYCLES cycles per launch, so cycles / median duration is the clock
+    the matrix pipes ran at; the probe's own counters (clock64 against the
+    constant-rate wall_clock64) give a second reading."""
+    import numpy as np
+    import torch
+
+    from tiled_fp32_gemm_amd import probe
+    words = probe.STAMP_WORDS * probe.WORKGROUPS
+    stamps = torch.zeros(words, dtype=torch.int64, device="cuda:0")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(repeats)]
+    for a, b in evs:
+        a.record(stream)
+        st = probe.mfma_clock(stream.cuda_stream, iters, stamps.data_ptr())
+        b.record(stream)
+        if st != 0:
+            raise RuntimeError(f"clock probe launch failed (status {st})")
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    cycles = iters * probe.MFMA_PER_ITER * (probe.WAVES // 4) * probe.MFMA_CYCLES
+    flops = (probe.WORKGROUPS * probe.WAVES * iters * probe.MFMA_PER_ITER
+             * 32 * 32 * 2 * 2)
+    v = probe.versions()
+    st = stamps.view(probe.WORKGROUPS, probe.STAMP_WORDS).cpu().numpy().astype(np.float64)
+    dw = st[:, 3] - st[:, 1]
+    counter_mhz = (float(np.median((st[:, 2] - st[:, 0]) / dw)) * v["wall_clock_khz"] / 1e3
+                   if np.all(dw > 0) else None)
+    return {"probe_ms": round(ms, 5),
+            "probe_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_clock_ghz": round(cycles / (ms * 1e-3) / 1e9, 4),
+            "clock64_mhz": None if counter_mhz is None else round(counter_mhz, 1),
+            "wall_clock_khz": v["wall_clock_khz"]}
+
+
+def versions() -> dict:
+    """ROCm, HIP runtime and driver, and torch versions of this run."""
+    import torch
+
+    from tiled_fp32_gemm_amd import probe
+    out = {"torch": torch.__version__, "torch_hip": torch.version.hip}
+    try:
+        out["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        out["rocm"] = None
+    v = probe.versions()
+    out["hip_runtime"] = v["hip_runtime"]
+    out["hip_driver"] = v["hip_driver"]
+    try:
+        out["amdgpu_module"] = open("/sys/module/amdgpu/version").read().strip()
+    except OSError:
+        out["amdgpu_module"] = None
+    return out
 
 
 def copy_calibration(nbytes: int) -> None:
@@ -163,7 +262,7 @@ def bench_transpose(args) -> int:
             raise sg.SgemmError(st, "sgemm_transpose_ex")
 
     def timed(fn):
-        timed.nwarm = warm_up(fn, args)
+        timed.nwarm = warm_up(fn, args)[0]
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -201,36 +300,43 @@ def bench_transpose(args) -> int:
     return 0
 
 
-def warm_up(fn, args) -> int:
-    """Untimed steps fn(0), fn(1), ...: exactly --warmup of them when given;
-    by default at least 20 and at least --warmup-seconds of device time, in
-    synchronised batches of 10, since an idle GPU takes tens of
-    milliseconds of work to reach its full clock.  Returns the count."""
+def warm_up(fn, args) -> tuple:
+    """Untimed launches fn(0), fn(1), ...: first a clock ramp, in synchronised
+    batches of 10, of at least 20 launches and at least --warmup-seconds (an
+    idle GPU takes tens of milliseconds of work to reach its full clock),
+    then the counted warm-up steps, --warmup of them (default 10).  Returns
+    (counted steps, ramp seconds, ramp launches)."""
     import torch
-    if args.warmup is not None:
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        return args.warmup
-    n, t0 = 0, time.perf_counter()
-    while n < 20 or time.perf_counter() - t0 < args.warmup_seconds:
+    ramp, t0 = 0, time.perf_counter()
+    while ramp < 20 or time.perf_counter() - t0 < args.warmup_seconds:
         for _ in range(10):
-            fn(n)
-            n += 1
+            fn(ramp)
+            ramp += 1
         torch.cuda.synchronize()
-    return n
+    ramp_s = time.perf_counter() - t0
+    w = 10 if args.warmup is None else args.warmup
+    for i in range(w):
+        fn(ramp + i)
+    torch.cuda.synchronize()
+    return w, ramp_s, ramp
+
+
+def event_stride(steps: int, every: int) -> int:
+    """Every how many timed steps one is event-timed: --event-every, lowered
+    so that at least min(10, steps) launches are."""
+    return max(1, min(every, steps // 10))
 
 
 def timed_steps(step, args, stream):
     """Warms up (warm_up), then runs --steps timed steps between two device
-    synchronisations, every --event-every-th also between two HIP events on
+    synchronisations, every event_stride()-th also between two HIP events on
     stream.  Returns (wall seconds, event-timed milliseconds of the sampled
-    steps, warm-up steps)."""
+    steps, warm_up's result)."""
     import numpy as np
     import torch
-    nwarm = warm_up(lambda i: step(), args)
-    steps, every = args.steps, args.event_every
-    every = max(1, every)
+    warm = warm_up(lambda i: step(), args)
+    steps = args.steps
+    every = event_stride(steps, args.event_every)
     timed = [i for i in range(steps) if i % every == every // 2] or [0]
     starts = {i: torch.cuda.Event(enable_timing=True) for i in timed}
     ends = {i: torch.cuda.Event(enable_timing=True) for i in timed}
@@ -245,7 +351,7 @@ def timed_steps(step, args, stream):
             step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, np.array([starts[i].elapsed_time(ends[i]) for i in timed]), nwarm
+    return wall, np.array([starts[i].elapsed_time(ends[i]) for i in timed]), warm
 
 
 def bench_ws(args) -> int:
@@ -285,7 +391,8 @@ def bench_ws(args) -> int:
         if st != sg.OK:
             raise sg.SgemmError(st, "sgemm")
 
-    wall, ev_ms, nwarm = timed_steps(step_ws, args, stream)
+    wall, ev_ms, warm = timed_steps(step_ws, args, stream)
+    nwarm = warm[0]
     wall_p, ev_p, _ = timed_steps(step_plain, args, stream)
     flops = 2.0 * M * N * K
     achieved = flops / (float(ev_ms.mean()) / 1e3) / 1e12
@@ -427,7 +534,7 @@ def bench_ladder(args) -> int:
                                  tC.data_ptr(), N, sh)
             if st != sg.OK:
                 raise sg.SgemmError(st, "sgemm_ladder")
-        nwarm = warm_up(lambda i: run(), args)
+        nwarm, _, ramp_n = warm_up(lambda i: run(), args)
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -451,6 +558,7 @@ def bench_ladder(args) -> int:
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": f"sgemm {args.workload}: M={M} N={N} K={K}",
                        "ladder_step": step, "name": name,
+                       "clock_ramp_launches": ramp_n,
                        "kernel_ms_median": round(float(np.median(ev_ms)), 5),
                        "max_rel_diff_vs_sgemm": rel},
             "roofline": {"bound": "mfma" if name.startswith("mfma") else "alu",
@@ -468,9 +576,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps (default: at least 20 and at least "
-                         "--warmup-seconds of device time)")
-    ap.add_argument("--warmup-seconds", type=float, default=0.3)
+                    help="counted untimed steps after the clock ramp (default 10)")
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="clock ramp before the warm-up steps: launches for at "
+                         "least this long (and at least 20)")
     ap.add_argument("--workload", default="4096cube", choices=sorted(WORKLOADS))
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "fma", "simple"])
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -479,7 +588,8 @@ def main() -> int:
                     help="repeat the CPU oracle sample until this much time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=10, metavar="N",
-                    help="time every N-th launch of the timed steps with HIP events")
+                    help="time every N-th launch of the timed steps with HIP "
+                         "events (lowered so that at least min(10, steps) are)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--shapes", default=None,
                     help="--op vendor: comma-separated MxNxK list instead of the built-in one")
@@ -555,7 +665,8 @@ def main() -> int:
         if st != sg.OK:
             raise sg.SgemmError(st, "sgemm_ex")
 
-    wall, ev_ms, nwarm = timed_steps(step, args, stream)
+    wall, ev_ms, (nwarm, ramp_s, ramp_n) = timed_steps(step, args, stream)
+    clock = clock_probe(stream)
 
     flops = 2.0 * M * N * K
     value = flops * args.steps / wall / 1e12
@@ -594,6 +705,12 @@ def main() -> int:
                                   round(float(np.percentile(ev_ms, 90)), 5)],
             "source_hash": src_hash,
             "device": torch.cuda.get_device_name(dev),
+            "arch": torch.cuda.get_device_properties(dev).gcnArchName,
+            "clock_ramp_s": round(ramp_s, 3),
+            "clock_ramp_launches": ramp_n,
+            "clock": clock,
+            "inputs_sha256": seedgen.sha256_of(A, B),
+            "versions": versions(),
         },
         "roofline": {
             "bound": "mfma",
@@ -605,11 +722,19 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    status = 0
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_rows,
-                                           args.cpu_seconds)
+        out["cpu_baseline"], check = cpu_baseline(
+            A, B, M, N, K, args.cpu_rows, args.cpu_seconds,
+            lambda r: tC[:r].cpu().numpy())
+        out["config"]["max_err_norm"] = check["max_err_norm"]
+        out["config"]["check"] = check
+        if not check["ok"]:
+            status = 3
+            print(f"bench.py: the GPU product is out of tolerance against the "
+                  f"oracle: {check}", file=sys.stderr)
     print(json.dumps(out), flush=True)
-    return 0
+    return status
 
 
 if __name__ == "__main__":

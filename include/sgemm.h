@@ -45,8 +45,16 @@
  *                          null or misaligned (not 4-byte) pointer for a
  *                          non-empty operand; C overlapping A or B; an
  *                          unknown algo.
- *   SGEMM_ERR_UNSUPPORTED  an operand spans 2 GiB or more (the kernels
- *                          address each operand with 32-bit byte offsets).
+ *   SGEMM_ERR_UNSUPPORTED  M, N or K of 2^31 - 1024 or more; or, for every
+ *                          tile the kernel family offers, one tile's rows
+ *                          of A or of C, or one K slab's rows of B, would
+ *                          span 2 GiB or more (the kernels address an
+ *                          operand from the corner of their own tile with
+ *                          32-bit byte offsets, so operands themselves may
+ *                          be of any size: this needs a leading dimension
+ *                          of millions of floats, e.g. lda >= 2^24 with 32
+ *                          or more rows of A); or a grid of 2^32 work-items
+ *                          or more.  sgemm_plan_query answers the same.
  *   SGEMM_ERR_LAUNCH       the HIP launch reported an error.
  * M == 0 or N == 0 returns SGEMM_OK with nothing enqueued; K == 0 writes
  * C = 0 (the empty sum).
@@ -158,7 +166,8 @@ int sgemm_plan_query(int64_t M, int64_t N, int64_t K,
  * sgemm(), bit for bit, and the workspace is not touched.
  *   workspace        device memory owned by the caller, 4-byte aligned, not
  *                    overlapping A, B or C; its contents on entry do not
- *                    matter and are overwritten (S x M x N floats).  It must
+ *                    matter and are overwritten (S x M x N floats; a split
+ *                    is only planned while these stay below 2 GiB).  It must
  *                    stay allocated until the enqueued kernels finish, and
  *                    calls that share one workspace must be ordered (one
  *                    stream), or they race.  May be NULL when
@@ -197,7 +206,9 @@ int sgemm_plan_query_ws(int64_t M, int64_t N, int64_t K,
  * the caller, 4-byte aligned, not
  * overlapping; any leading dimension; enqueued on stream without
  * synchronising.  Errors as for sgemm (checked before any HIP call);
- * rows == 0 or cols == 0 is a no-op. */
+ * rows == 0 or cols == 0 is a no-op; SGEMM_ERR_UNSUPPORTED when rows or cols
+ * is 2^31 - 1024 or more, when 64 input rows or 128 output rows would span
+ * 2 GiB or more, or when the grid would reach 2^32 work-items. */
 int sgemm_transpose(int64_t rows, int64_t cols,
                     const float *in, int64_t ldi,
                     float *out, int64_t ldo,

@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgemm.h")
 
 BIG = 1 << 33  # a plausible, 16-byte aligned fake device address
+FAR_B, FAR_C = BIG + (1 << 40), BIG + (1 << 41)   # past any operand at BIG
 
 
 @pytest.fixture(scope="module")
@@ -35,6 +36,25 @@ def test_header_declares_the_binding_names():
 def test_every_declared_symbol_is_exported(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
+
+
+def test_probe_library_exports_its_header():
+    # the benchmark's measurement aids: a library and header of their own
+    import ctypes
+
+    from tiled_fp32_gemm_amd import build, probe
+    build.ensure_built()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sgemm_probe.h")).read(),
+                  flags=re.S)
+    names = re.findall(r"^\s*int\s+(\w+)\s*\(", text, re.M)
+    assert sorted(names) == ["sgemm_probe_mfma_clock", "sgemm_probe_versions"]
+    plib = ctypes.CDLL(build.PROBE_LIB)
+    for name in names:
+        assert hasattr(plib, name), name
+    # argument checks answered before any HIP call
+    assert probe.mfma_clock(0, 0, 1 << 33) == 1
+    assert probe.mfma_clock(0, 16, 0) == 1
+    assert probe.mfma_clock(0, 16, (1 << 33) + 4) == 1
 
 
 def test_one_hip_runtime_is_mapped(lib):
@@ -77,8 +97,12 @@ def call(M, N, K, A=BIG, lda=None, B=BIG + (1 << 31), ldb=None,
     (dict(M=4, N=4, K=4, B=BIG + (1 << 32) + 60), sg.ERR_INVALID_ARG),  # B overlaps C
     (dict(M=4, N=4, K=4, algo=5), sg.ERR_INVALID_ARG),
     (dict(M=4, N=4, K=4, algo=-1), sg.ERR_INVALID_ARG),
-    (dict(M=1 << 15, N=4, K=1 << 14), sg.ERR_UNSUPPORTED),  # A spans 2 GiB
-    (dict(M=(1 << 31) // 4096 + 1, N=1024, K=4, ldc=1024), sg.ERR_UNSUPPORTED),
+    # operands far apart, so that only the size limits can reject
+    (dict(M=(1 << 31) - 1023, N=4, K=4, B=FAR_B, C=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(M=64, N=4, K=8, lda=1 << 25, B=FAR_B, C=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(M=4, N=4, K=64, ldb=1 << 26, B=FAR_B, C=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(M=64, N=4, K=4, ldc=1 << 26, B=FAR_B, C=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(M=(1 << 29) - 1, N=1, K=1, algo=1, B=FAR_B, C=FAR_C), sg.ERR_UNSUPPORTED),
 ])
 def test_rejected_before_any_hip_call(lib, args, status):
     st, _ = call(**args)
@@ -157,7 +181,12 @@ def test_plans_per_family(lib):
     (dict(rows=4, cols=4, out=BIG + 2), sg.ERR_INVALID_ARG),
     (dict(rows=4, cols=4, out=BIG + 32), sg.ERR_INVALID_ARG),  # overlap
     (dict(rows=4, cols=4, layout=4), sg.ERR_INVALID_ARG),
-    (dict(rows=1 << 16, cols=1 << 13), sg.ERR_UNSUPPORTED),  # 2 GiB
+    # one tile's input rows (64) or output rows (128) spanning 2 GiB or
+    # more, a dimension past the limit, a grid of 2^32 work-items
+    (dict(rows=64, cols=4, ldi=1 << 25, out=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(rows=4, cols=128, ldo=1 << 25, out=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(rows=(1 << 31) - 1023, cols=1, out=FAR_C), sg.ERR_UNSUPPORTED),
+    (dict(rows=(1 << 31) - 1024, cols=1, out=FAR_C), sg.ERR_UNSUPPORTED),
     (dict(rows=0, cols=4, inp=0, out=0), sg.OK),
 ])
 def test_transpose_checks(lib, args, status):

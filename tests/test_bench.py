@@ -48,17 +48,38 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr and not r.stdout.strip()
 
 
+def test_event_stride_keeps_at_least_ten_samples():
+    sys.path.insert(0, ROOT)
+    import bench
+    for steps in (1, 5, 10, 19, 20, 37, 100, 200, 1000):
+        for every in (1, 3, 10, 50):
+            k = bench.event_stride(steps, every)
+            sampled = [i for i in range(steps) if i % k == k // 2] or [0]
+            assert len(sampled) >= min(10, steps), (steps, every)
+            assert k <= every
+
+
 @pytest.mark.gpu
 def test_gemm_line(capsys):
-    rc, lines = run_main(["--steps", "4", "--warmup", "1", "--workload", "256cube",
-                          "--cpu-seconds", "0.05", "--cpu-rows", "8"], capsys)
+    rc, lines = run_main(["--steps", "20", "--warmup", "1", "--workload", "256cube",
+                          "--cpu-seconds", "0.05", "--cpu-rows", "256"], capsys)
     assert rc == 0 and len(lines) == 1
     d = lines[0]
-    check_line(d, 4, 1)
+    check_line(d, 20, 1)
     assert d["roofline"]["bound"] == "mfma" and d["roofline"]["peak"] == 157.3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
-    assert d["config"]["event_timed_launches"] >= 1
+    assert set(cb["one_core"]) == {"256cube", "ragged"}
+    cfg = d["config"]
+    assert cfg["event_timed_launches"] >= 10
+    assert cfg["clock_ramp_s"] >= 0.3 and cfg["clock_ramp_launches"] >= 20
+    # the whole 256^3 product checked against the oracle
+    assert cfg["check"]["ok"] and cfg["check"]["elements"] == 256 * 256
+    assert 0 <= cfg["max_err_norm"] <= 1e-5
+    assert len(cfg["inputs_sha256"]) == 64
+    # a matrix-core clock between 1 and 3 GHz, and versions recorded
+    assert 1.0 < cfg["clock"]["mfma_clock_ghz"] < 3.0
+    assert cfg["versions"]["hip_runtime"] > 0
 
 
 @pytest.mark.gpu

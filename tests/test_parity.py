@@ -238,33 +238,6 @@ def test_k_zero_writes_zeros_and_empty_is_noop(algo):
     assert np.all(dC2.host() == 5.0)
 
 
-@pytest.mark.parametrize("K", [16383, 16380])
-def test_largest_operand(K):
-    """A just under the 2 GiB operand limit (integer data made on the GPU);
-    sampled rows, including the last, against the oracle, bit-exact.  K =
-    16383 takes the register-staged path, K = 16380 the LDS-direct one."""
-    M, N = 32768, 64
-    say(f"[gpu] largest operand: A {M}x{K} ({M * K * 4 / 2**30:.4f} GiB)")
-    i = torch.arange(M, device="cuda:0", dtype=torch.int64)[:, None]
-    k = torch.arange(K, device="cuda:0", dtype=torch.int64)[None, :]
-    dA = ((i * 7 + k * 3) % 17 - 8).to(torch.float32).contiguous()
-    B = seedgen.integer_matrix(K, N, -8, 8, 4242)
-    dB = torch.from_numpy(B).to("cuda:0")
-    dC = torch.full((M, N), float("nan"), device="cuda:0")
-    import tiled_fp32_gemm_amd as sg
-    st = sg.sgemm(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
-                  torch.cuda.current_stream().cuda_stream)
-    assert st == sg.OK
-    torch.cuda.synchronize()
-    rows = np.array([0, 1, 4095, 4096, 20000, M - 2, M - 1])
-    Arows = dA[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
-    Cref, _ = oracle.gemm(Arows, B, with_t=False)
-    got = dC[torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
-    assert np.array_equal(got, Cref.astype(np.float32))
-    assert bool(torch.isfinite(dC).all())
-    del dA, dC
-
-
 # One shape per LDS-direct variant the planner can pick (the test checks the
 # pick), each with K not a multiple of 4 so that the straddling A groups are
 # zero-filled, and with an odd lda so that A rows are only 4-byte aligned.

@@ -1,4 +1,5 @@
-"""Builds libsgemm.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Builds libsgemm.so (the HIP kernels and the C ABI) and libsgemm_probe.so
+(the benchmark's clock probe) for gfx950 with hipcc.
 
 ``python -m tiled_fp32_gemm_amd.build [--asm]`` compiles in-tree; ``--asm``
 also writes the device assembly next to the sources' build folder
@@ -14,6 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsgemm.so")
+PROBE_LIB = os.path.join(HERE, "libsgemm_probe.so")
 ROOT = os.path.dirname(HERE)
 ASM_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
@@ -28,20 +30,25 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17",
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) +
                   glob.glob(os.path.join(CSRC, "*.hpp")) +
-                  [os.path.join(ROOT, "include", "sgemm.h")])
+                  glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile ``csrc/sgemm.hip`` into ``libsgemm.so`` (always recompiles)."""
-    tmp = LIB + f".tmp{os.getpid()}"
+def _compile(src: str, out: str, verbose: bool) -> str:
+    tmp = out + f".tmp{os.getpid()}"
     cmd = ["hipcc", *DEVICE_FLAGS, "-fPIC", "-shared",
-           "-Wl,-rpath,/opt/rocm/lib",
-           os.path.join(CSRC, "sgemm.hip"), "-o", tmp]
+           "-Wl,-rpath,/opt/rocm/lib", src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``csrc/sgemm.hip`` into ``libsgemm.so`` and ``csrc/probe.hip``
+    into ``libsgemm_probe.so`` (always recompiles)."""
+    _compile(os.path.join(CSRC, "probe.hip"), PROBE_LIB, verbose)
+    return _compile(os.path.join(CSRC, "sgemm.hip"), LIB, verbose)
 
 
 def build_asm() -> str:
@@ -55,9 +62,10 @@ def build_asm() -> str:
 
 
 def ensure_built() -> str:
-    """Build only when the library is missing or older than a source."""
-    if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(
-            os.path.getmtime(s) for s in sources()):
+    """Build only when a library is missing or older than a source."""
+    newest = max(os.path.getmtime(s) for s in sources())
+    if any(not os.path.exists(p) or os.path.getmtime(p) < newest
+           for p in (LIB, PROBE_LIB)):
         return build()
     return LIB
 

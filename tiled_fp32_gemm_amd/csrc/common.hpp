@@ -1,12 +1,18 @@
 // common.hpp -- device helpers shared by the gfx950 SGEMM kernels.
 //
 // Buffer resources.  Every operand is read and written through a raw buffer
-// resource (base, byte size).  A lane whose element lies outside the logical
-// matrix is given the byte offset kOob, which is past the end of any resource
-// the host accepts (operands are < 2 GiB), so its load returns 0 and its store
-// is dropped by the hardware range check.  That is the pages' predicated edge
-// load that writes 0 for invalid elements ("CUDA in depth (5)", section on
-// edges), without a branch, and no stale value is ever multiplied by 0.
+// resource (base, byte size).  A kernel does not address a whole operand from
+// its first element: it moves the base to the corner of its own C tile (A to
+// the tile's first row, C to its first row and column, B to its first column
+// and, slab by slab, to the slab's first row), so that every byte offset a
+// lane forms stays below 2^31 however large the operand is; the host checks
+// that one tile's rows (one slab's rows for B) span less than 2 GiB.  A
+// resource is never larger than 2^31 bytes, and a lane whose element lies
+// outside the logical matrix is given the byte offset kOob = 2^31, past its
+// end, so its load returns 0 and its store is dropped by the hardware range
+// check.  That is the pages' predicated edge load that writes 0 for invalid
+// elements ("CUDA in depth (5)", section on edges), without a branch, and no
+// stale value is ever multiplied by 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,6 +28,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // swizzle, stride 0) addressing.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int64_t kRsrcMax = int64_t(1) << 31;  // bytes; kOob is past the end
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
                                                           uint32_t bytes) {
@@ -51,6 +58,17 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                          0, 0);
 }
 
+// A resource over an operand of `bytes` bytes starting at `base`, moved
+// `skip` floats forward: the rest of the operand, capped at kRsrcMax bytes
+// (empty when nothing is left).  All arguments are wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const float* base,
+                                                        int64_t bytes,
+                                                        int64_t skip) {
+  const int64_t rem = bytes - 4 * skip;
+  const uint32_t n = rem <= 0 ? 0u : (rem >= kRsrcMax ? (uint32_t)kRsrcMax : (uint32_t)rem);
+  return make_rsrc(base + skip, n);
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l's data lands
 // at lds_dst + 16 l bytes (lds_dst must be the same for the whole wave);
 // out-of-range lanes write zeros.
@@ -60,13 +78,15 @@ __device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r,
       r, (__attribute__((address_space(3))) void*)lds_dst, 16, off, 0, 0, 0);
 }
 
-// Kernel arguments, identical for every family.  Sizes are checked on the host
-// (M, N, K >= 0, every operand < 2 GiB), so 32-bit byte offsets suffice.
+// Kernel arguments, identical for every family.  Sizes are checked on the
+// host: 0 <= M, N, K < 2^31 - 1024 (so tile origins stay in int range) and one
+// tile's rows of A and C, and one slab's rows of B, span less than 2 GiB, so
+// 32-bit byte offsets from a tile's corner suffice.
 struct GemmArgs {
   const float* A;
   const float* B;
   float* C;
-  uint32_t a_bytes, b_bytes, c_bytes;  // resource sizes
+  int64_t a_bytes, b_bytes, c_bytes;   // bytes each operand spans
   int M, N, K;
   int lda, ldb, ldc;
   int tiles_m, tiles_n;                // C tiles along M and N

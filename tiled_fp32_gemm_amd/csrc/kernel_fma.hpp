@@ -61,9 +61,14 @@ sgemm_fma_kernel(GemmArgs g) {
   const int lane = tid & 63, wave = tid >> 6;
   const int tx = lane & 15, ty = 4 * wave + (lane >> 4);
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+  // The tile's corner of each operand (A from row m0, B from column n0, C
+  // from (m0, n0)); each slab moves A and B on to its own first column and
+  // row, so lane offsets are counted from the slab's corner.
+  const float* const At = g.A + (int64_t)m0 * g.lda;
+  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const float* const Bt = g.B + n0;
+  const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
+  const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
 
   // A slot: row (f % 16) + 16 (f / 64), k group (f / 16) % 4, f = s NT + tid.
   uint32_t a_off[Cfg::A_SLOTS];
@@ -75,8 +80,8 @@ sgemm_fma_kernel(GemmArgs g) {
     const int row = (f & 15) + ((f >> 6) << 4), kq = (f >> 4) & 3;
     a_row[s] = row;
     a_k[s] = 4 * kq;
-    a_row_ok[s] = (m0 + row) < g.M;
-    a_off[s] = ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * kq) * 4u;
+    a_row_ok[s] = row < g.M - m0;
+    a_off[s] = ((uint32_t)row * (uint32_t)g.lda + 4u * kq) * 4u;
   }
   uint32_t b_off[Cfg::B_SLOTS];
   int b_k[Cfg::B_SLOTS], b_j[Cfg::B_SLOTS], b_lds[Cfg::B_SLOTS];
@@ -86,16 +91,18 @@ sgemm_fma_kernel(GemmArgs g) {
     const int k = f / (BN / 4), jq = f % (BN / 4);
     b_k[s] = k;
     b_j[s] = n0 + 4 * jq;
-    b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * jq)) * 4u;
+    b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(4 * jq)) * 4u;
     b_lds[s] = k * RB + 4 * jq;
   }
 
   f32x4 sa[Cfg::A_SLOTS], sb[Cfg::B_SLOTS];
   auto load_slab = [&](int k0) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
       const int k = k0 + a_k[s];
-      const uint32_t base = a_off[s] + (uint32_t)k0 * 4u;
+      const uint32_t base = a_off[s];
       if constexpr (VEC_A) {
         sa[s] = load4(ra, (a_row_ok[s] && k < g.K) ? base : kOob);
       } else {
@@ -107,7 +114,7 @@ sgemm_fma_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < Cfg::B_SLOTS; ++s) {
       const bool k_ok = (k0 + b_k[s]) < g.K;
-      const uint32_t base = b_off[s] + (uint32_t)k0 * (uint32_t)g.ldb * 4u;
+      const uint32_t base = b_off[s];
       if constexpr (VEC_B) {
         sb[s] = load4(rb, (k_ok && b_j[s] < g.N) ? base : kOob);
       } else {
@@ -165,24 +172,25 @@ sgemm_fma_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // Epilogue: row 4ty + i (+64) and columns 4tx..4tx+3 (+64); a quarter-wave
-  // writes 256 contiguous bytes of one row.
+  // Epilogue: row 4ty + i (+64) and columns 4tx..4tx+3 (+64) from the
+  // tile's corner; a quarter-wave writes 256 contiguous bytes of one row.
+  const int m_left = g.M - m0, n_left = g.N - n0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = m0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + i - 4);
-    const bool row_ok = row < g.M;
+    const int row = i < 4 ? 4 * ty + i : 64 + 4 * ty + i - 4;
+    const bool row_ok = row < m_left;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int col = n0 + 64 * h + 4 * tx;
+      const int col = 64 * h + 4 * tx;
       const uint32_t off = ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u;
       if constexpr (VEC_C) {
         const f32x4 v = {acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2],
                          acc[i][4 * h + 3]};
-        store4(rc, (row_ok && col < g.N) ? off : kOob, v);
+        store4(rc, (row_ok && col < n_left) ? off : kOob, v);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          store1(rc, (row_ok && col + e < g.N) ? off + 4u * e : kOob,
+          store1(rc, (row_ok && col + e < n_left) ? off + 4u * e : kOob,
                  acc[i][4 * h + e]);
       }
     }

@@ -53,18 +53,28 @@ __global__ void __launch_bounds__(256) sgemm_naive_kernel(GemmArgs g) {
   int tm, tn;
   tile_of_workgroup(g, tm, tn);
   const int tx = (int)threadIdx.x & 15, ty = (int)threadIdx.x >> 4;
-  const int row = tm * 16 + ty, col = tn * 16 + tx;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+  const int m0 = tm * 16, n0 = tn * 16;
+  const int row = m0 + ty, col = n0 + tx;
+  // The tile's corner of A (row m0), B (column n0) and C (m0, n0); A and B
+  // move on by 16 values of k at a time.
+  const float* const At = g.A + (int64_t)m0 * g.lda;
+  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const float* const Bt = g.B + n0;
+  const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
+  const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
   const bool row_ok = row < g.M, col_ok = col < g.N;
   float sum = 0.0f;
-  for (int k = 0; k < g.K; ++k) {
-    const float a = load1(ra, row_ok ? ((uint32_t)row * (uint32_t)g.lda + (uint32_t)k) * 4u : kOob);
-    const float b = load1(rb, col_ok ? ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)col) * 4u : kOob);
-    sum = __builtin_fmaf(a, b, sum);
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
+    const int kn = min(16, g.K - k0);
+    for (int k = 0; k < kn; ++k) {
+      const float a = load1(ra, row_ok ? ((uint32_t)ty * (uint32_t)g.lda + (uint32_t)k) * 4u : kOob);
+      const float b = load1(rb, col_ok ? ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)tx) * 4u : kOob);
+      sum = __builtin_fmaf(a, b, sum);
+    }
   }
-  store1(rc, (row_ok && col_ok) ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob, sum);
+  store1(rc, (row_ok && col_ok) ? ((uint32_t)ty * (uint32_t)g.ldc + (uint32_t)tx) * 4u : kOob, sum);
 }
 
 enum LadderALayout { kAUnpadded = 0, kAPadded = 1, kASwizzled = 2 };
@@ -114,9 +124,13 @@ sgemm_ladder_kernel(GemmArgs g) {
   const int lane = tid & 63, wave = tid >> 6;
   const int tx = lane & 15, ty = 4 * wave + (lane >> 4);
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+  // The tile's corner of A (row m0), B (column n0) and C (m0, n0); each
+  // slab moves A and B on to its own first column and row.
+  const float* const At = g.A + (int64_t)m0 * g.lda;
+  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const float* const Bt = g.B + n0;
+  const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
+  const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
 
   // Column of As that holds tile row r at slab depth k.
   auto a_col = [](int r, int k) {
@@ -131,6 +145,8 @@ sgemm_ladder_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
 
   for (int k0 = 0; k0 < g.K; k0 += BK) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
     // A group f: tile row (f % 16) + 16 (f / 64), k quad (f / 16) % 4.
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
@@ -138,7 +154,7 @@ sgemm_ladder_kernel(GemmArgs g) {
       if (f < Cfg::A_GROUPS) {
         const int row = (f & 15) + ((f >> 6) << 4), kq = (f >> 4) & 3;
         const int gr = m0 + row, gk = k0 + 4 * kq;
-        const uint32_t off = ((uint32_t)gr * (uint32_t)g.lda + (uint32_t)gk) * 4u;
+        const uint32_t off = ((uint32_t)row * (uint32_t)g.lda + (uint32_t)(4 * kq)) * 4u;
         f32x4 v;
         if constexpr (VEC) {
           v = load4(ra, (gr < g.M && gk < g.K) ? off : kOob);
@@ -158,7 +174,7 @@ sgemm_ladder_kernel(GemmArgs g) {
       if (f < Cfg::B_GROUPS) {
         const int k = f / (BN / 4), jq = f % (BN / 4);
         const int gk = k0 + k, gc = n0 + 4 * jq;
-        const uint32_t off = ((uint32_t)gk * (uint32_t)g.ldb + (uint32_t)gc) * 4u;
+        const uint32_t off = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(4 * jq)) * 4u;
         f32x4 v;
         if constexpr (VEC) {
           v = load4(rb, (gk < g.K && gc < g.N) ? off : kOob);
@@ -218,27 +234,28 @@ sgemm_ladder_kernel(GemmArgs g) {
   // Row i of the thread: group i / RG, offset i % RG; columns alike.  With 4
   // columns per group and aligned rows of C a group is one 128-bit store.
   const bool vc = (((uintptr_t)g.C & 15u) == 0) && (g.ldc % 4 == 0) && (g.N % 4 == 0);
+  const int m_left = g.M - m0, n_left = g.N - n0;   // rows, columns from the corner
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int row = m0 + (i / RG) * 16 * RG + RG * ty + i % RG;
-    const bool row_ok = row < g.M;
+    const int row = (i / RG) * 16 * RG + RG * ty + i % RG;
+    const bool row_ok = row < m_left;
 #pragma unroll
     for (int gj = 0; gj < Cfg::NGN; ++gj) {
-      const int col = n0 + gj * 16 * CG + CG * tx;
+      const int col = gj * 16 * CG + CG * tx;
       const uint32_t off = ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u;
       bool done = false;
       if constexpr (CG == 4) {
         if (vc) {
           const f32x4 v = {acc[i][4 * gj], acc[i][4 * gj + 1], acc[i][4 * gj + 2],
                            acc[i][4 * gj + 3]};
-          store4(rc, (row_ok && col < g.N) ? off : kOob, v);
+          store4(rc, (row_ok && col < n_left) ? off : kOob, v);
           done = true;
         }
       }
       if (!done) {
 #pragma unroll
         for (int e = 0; e < CG; ++e)
-          store1(rc, (row_ok && col + e < g.N) ? off + 4u * e : kOob, acc[i][gj * CG + e]);
+          store1(rc, (row_ok && col + e < n_left) ? off + 4u * e : kOob, acc[i][gj * CG + e]);
       }
     }
   }

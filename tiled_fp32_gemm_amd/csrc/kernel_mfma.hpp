@@ -12,7 +12,10 @@
 //    multiply-add, accumulators in registers).
 //  * Global -> registers: 128-bit buffer loads (VEC_A / VEC_B) or, when a row
 //    is not 16-byte aligned, four 32-bit loads per 4-float group; elements
-//    outside the matrix read as 0 through the buffer range check.
+//    outside the matrix read as 0 through the buffer range check.  Each slab
+//    reads through resources moved to its own corner (A: the tile's first
+//    row and the slab's first column; B: the slab's first row and the tile's
+//    first column), so the per-lane offsets do not grow with K.
 //  * Registers -> LDS, double buffered: the loads for slab t+1 are issued
 //    before the matrix instructions of slab t and written to the other LDS
 //    stage after them, with one barrier per slab.
@@ -115,11 +118,16 @@ sgemm_mfma_kernel(GemmArgs g) {
   const int wn0 = (sw % Cfg::WAVES_N) * WN;
   const int li = lane & 31, lh = lane >> 5;
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, g.b_bytes);
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+  // The tile's corner of each operand (A from row m0, B from column n0, C
+  // from (m0, n0)); rows and columns below are counted from there.
+  const float* const At = g.A + (int64_t)m0 * g.lda;
+  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const float* const Bt = g.B + n0;
+  const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
+  const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
 
-  // Per-slot global byte offsets at k0 = 0 and the LDS positions they fill.
+  // Per-slot byte offsets from a slab's corner and the LDS positions they
+  // fill.
   uint32_t a_off[Cfg::A_SLOTS];
   bool a_row_ok[Cfg::A_SLOTS];
   int a_k[Cfg::A_SLOTS], a_lds[Cfg::A_SLOTS];
@@ -127,9 +135,9 @@ sgemm_mfma_kernel(GemmArgs g) {
   for (int s = 0; s < Cfg::A_SLOTS; ++s) {
     int row, kq;
     a_slot<Cfg>(s * NT + tid, row, kq);
-    a_row_ok[s] = (m0 + row) < g.M;
+    a_row_ok[s] = row < g.M - m0;
     a_k[s] = 4 * kq;
-    a_off[s] = ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * kq) * 4u;
+    a_off[s] = ((uint32_t)row * (uint32_t)g.lda + 4u * kq) * 4u;
     a_lds[s] = row * RA + 4 * kq;
   }
   uint32_t b_off[Cfg::B_SLOTS];
@@ -140,18 +148,20 @@ sgemm_mfma_kernel(GemmArgs g) {
     const int k = f / (BN / 4), jq = f % (BN / 4);
     b_k[s] = k;
     b_j[s] = n0 + 4 * jq;
-    b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * jq)) * 4u;
+    b_off[s] = ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(4 * jq)) * 4u;
     b_lds[s] = k * RB + 4 * jq;
   }
 
   f32x4 sa[Cfg::A_SLOTS], sb[Cfg::B_SLOTS];
 
-  // Global -> registers for the slab starting at k0.
+  // Global -> registers for the slab starting at k0 (< K).
   auto load_slab = [&](int k0) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {
       const int k = k0 + a_k[s];
-      const uint32_t base = a_off[s] + (uint32_t)k0 * 4u;
+      const uint32_t base = a_off[s];
       if constexpr (VEC_A) {
         sa[s] = load4(ra, (a_row_ok[s] && k < g.K) ? base : kOob);
       } else {
@@ -163,7 +173,7 @@ sgemm_mfma_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < Cfg::B_SLOTS; ++s) {
       const bool k_ok = (k0 + b_k[s]) < g.K;
-      const uint32_t base = b_off[s] + (uint32_t)k0 * (uint32_t)g.ldb * 4u;
+      const uint32_t base = b_off[s];
       if constexpr (VEC_B) {
         sb[s] = load4(rb, (k_ok && b_j[s] < g.N) ? base : kOob);
       } else {
@@ -268,18 +278,19 @@ sgemm_mfma_kernel(GemmArgs g) {
     }
   }
 
-  // Epilogue: each lane writes column n0 + wn0 + 32 j + li of 16 rows per
-  // block; lanes 0-31 cover 128 contiguous bytes of one row.
+  // Epilogue: each lane writes column wn0 + 32 j + li (from the tile's
+  // corner) of 16 rows per block; lanes 0-31 cover 128 contiguous bytes of
+  // one row.
 #pragma unroll
   for (int i = 0; i < TA; ++i) {
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
-      const int col = n0 + wn0 + 32 * j + li;
-      const bool col_ok = col < g.N;
+      const int col = wn0 + 32 * j + li;
+      const bool col_ok = col < g.N - n0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const bool ok = col_ok && row < g.M;
+        const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const bool ok = col_ok && row < g.M - m0;
         store1(rc, ok ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob,
                acc[i][j][r]);
       }

@@ -13,12 +13,15 @@
 // 4-byte-aligned address and range-checks each 4-byte word against the
 // resource, so rows of any alignment and leading dimension are loaded as
 // whole 4-float groups.  A lane's offset inside a slab never changes: each
-// slab moves the two resources instead (A's base by k0 columns, B's by k0
-// rows, their sizes shrunk to match), so a load is one instruction with no
+// slab moves the two resources instead (A's base to the tile's first row and
+// the slab's first column, B's to the slab's first row and the tile's first
+// column, their sizes shrunk to match), so a load is one instruction with no
 // per-lane address arithmetic.  The range check then does the edges:
 //   * A groups of rows >= M and B groups starting at a column >= N get the
 //     offset kOob once, and read zeros in every slab;
-//   * B rows k >= K lie past the end of the moved B resource and read zeros;
+//   * B rows k >= K lie past the end of the moved B resource and read zeros
+//     (a row whose offset from the slab's first row would reach 2^31 can
+//     only be such a row, and gets kOob);
 //   * a B group reaching past column N-1 brings in values that only feed C
 //     columns >= N, which are never stored;
 //   * A words at k >= K of a row below M-1 are inside the allocation (the
@@ -148,12 +151,12 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     const int kb = split * g_in.k_split;
     g.K = min(g_in.k_split, g_in.K - kb);
     g.A = g_in.A + kb;
-    g.a_bytes = g_in.a_bytes - 4u * (uint32_t)kb;
-    g.B = g_in.B + (size_t)kb * (size_t)g_in.ldb;
-    g.b_bytes = g_in.b_bytes - 4u * (uint32_t)kb * (uint32_t)g_in.ldb;
-    g.C = g_in.W + (size_t)split * (size_t)g_in.M * (size_t)g_in.N;
+    g.a_bytes = g_in.a_bytes - 4 * (int64_t)kb;
+    g.B = g_in.B + (int64_t)kb * g_in.ldb;
+    g.b_bytes = g_in.b_bytes - 4 * (int64_t)kb * g_in.ldb;
+    g.C = g_in.W + (int64_t)split * g_in.M * g_in.N;
     g.ldc = g_in.N;
-    g.c_bytes = 4u * (uint32_t)g_in.M * (uint32_t)g_in.N;
+    g.c_bytes = 4 * (int64_t)g_in.M * g_in.N;
   } else {
     tile_of_workgroup(g, tm, tn);
   }
@@ -169,11 +172,18 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   const int wn0 = (sw % Cfg::WAVES_N) * WN;
   const int li = lane & 31, lh = lane >> 5;
 
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.C, g.c_bytes);
+  // The tile's corner of each operand: A from row m0, B from column n0, C
+  // from (m0, n0).  Rows and columns below are counted from there.
+  const float* const At = g.A + (int64_t)m0 * g.lda;
+  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const float* const Bt = g.B + n0;
+  const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
+  const int m_left = g.M - m0, n_left = g.N - n0;
+  const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
 
   // Unit u = s NT + 64 wave + lane of each load instruction, and the offset
-  // of the global 4-float group it takes in slab 0 (kOob when outside the
-  // matrix in M or N).  a_unit gives the row and k group of A slot s.
+  // of the global 4-float group it takes in every slab (kOob when outside
+  // the matrix in M or N).  a_unit gives the row and k group of A slot s.
   auto a_unit = [&](int s, int ln, int& row, int& c) {
     const int u = s * NT + 64 * wave + ln;
     row = (u / (16 * CPR)) * 16 + (u & 15);
@@ -184,31 +194,26 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   for (int s = 0; s < Cfg::A_SLOTS; ++s) {
     int row, c;
     a_unit(s, lane, row, c);
-    a_off[s] = (m0 + row) < g.M
-                   ? ((uint32_t)(m0 + row) * (uint32_t)g.lda + 4u * c) * 4u
-                   : kOob;
+    a_off[s] = row < m_left ? ((uint32_t)row * (uint32_t)g.lda + 4u * c) * 4u : kOob;
   }
   uint32_t b_off[Cfg::B_SLOTS];
 #pragma unroll
   for (int s = 0; s < Cfg::B_SLOTS; ++s) {
     const int u = s * NT + 64 * wave + lane;
     const int k = u / QB, q = (u % QB) ^ ((k & 8) ? 8 : 0);
-    b_off[s] = (n0 + 4 * q) < g.N
-                   ? ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(n0 + 4 * q)) * 4u
-                   : kOob;
+    // In floats from the slab's first row, formed in 64 bits: rows past a
+    // short K may lie 2^31 bytes or more away, and must read zeros, not wrap.
+    const uint64_t w = (uint64_t)k * (uint32_t)g.ldb + (uint32_t)(4 * q);
+    b_off[s] = (4 * q < n_left && w < (uint64_t)(kRsrcMax / 4)) ? (uint32_t)w * 4u : kOob;
   }
   // The resources of the slab starting at k0: A moved by k0 columns, B by
-  // k0 rows, each size shrunk to match.  Below K the shifts are smaller than
-  // the (sub-2 GiB) sizes, so 32-bit scalar arithmetic suffices; from K on
-  // the resource is empty and reads zeros.
+  // k0 rows, each size shrunk to match; from K on a resource is empty and
+  // reads zeros.
   auto rsrc_a = [&](int k0) {
-    const bool in = k0 < g.K;
-    return make_rsrc(in ? g.A + k0 : g.A, in ? g.a_bytes - 4u * (uint32_t)k0 : 0u);
+    return k0 < g.K ? rsrc_at(At, a_rem, k0) : make_rsrc(g.A, 0u);
   };
   auto rsrc_b = [&](int k0) {
-    const bool in = k0 < g.K;
-    const uint32_t sh = 4u * (uint32_t)k0 * (uint32_t)g.ldb;
-    return make_rsrc(in ? g.B + (size_t)(sh >> 2) : g.B, in ? g.b_bytes - sh : 0u);
+    return k0 < g.K ? rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb) : make_rsrc(g.B, 0u);
   };
 
   // Issue direct load l (the A slots, then the B slots) of a slab with
@@ -255,7 +260,7 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
       int row, c;
       a_unit(s, ln, row, c);
       const int k = t * BK + 4 * c;
-      if (k + 4 > g.K && m0 + row < g.M) {
+      if (k + 4 > g.K && row < m_left) {
         float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + ln);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -417,12 +422,12 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   for (int i = 0; i < TA; ++i) {
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
-      const int col = n0 + wn0 + 32 * j + li_c;
-      const bool col_ok = col < g.N;
+      const int col = wn0 + 32 * j + li_c;   // from the tile's corner
+      const bool col_ok = col < n_left;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * lh_c + (r & 3);
-        const bool ok = col_ok && row < g.M;
+        const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * lh_c + (r & 3);
+        const bool ok = col_ok && row < m_left;
         store1(rc, ok ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob,
                acc[i][j][r]);
       }

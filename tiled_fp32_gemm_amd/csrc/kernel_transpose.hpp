@@ -23,7 +23,8 @@
 // moved 8192^2 from 4.1 to 5.0 TB/s and 16384^2 from 4.6 to 5.1 TB/s on
 // MI355X, where a plain device copy reaches 4.7-5.3 TB/s.
 // Elements outside the matrix read as 0 and are not stored (buffer range
-// checks).  The unit layout is a template parameter, because it is the
+// checks); each tile reads and writes through resources moved to its own
+// corner, so offsets stay below 2^31 whatever the size of the matrices.  The unit layout is a template parameter, because it is the
 // experiment.  A 128-bit access is served 16 lanes at a time, and the 16
 // lanes of a read share c and e and differ in i:
 //
@@ -53,7 +54,7 @@ constexpr int kTransposeCols = 128;   // input columns per tile
 struct TransposeArgs {
   const float* in;
   float* out;
-  uint32_t in_bytes, out_bytes;
+  int64_t in_bytes, out_bytes;   // bytes each matrix spans
   int rows, cols;     // of the input
   int ldi, ldo;       // leading dimensions of input and output
   int tiles_x;        // tiles across the input's columns
@@ -85,8 +86,10 @@ __global__ void __launch_bounds__(256) sgemm_transpose_kernel(TransposeArgs a) {
   const int tx = (int)blockIdx.x % a.tiles_x, ty = (int)blockIdx.x / a.tiles_x;
   const int x0 = tx * kTransposeCols, y0 = ty * kTransposeRows;  // input column, row
   const int tid = (int)threadIdx.x;
-  const __amdgpu_buffer_rsrc_t rin = make_rsrc(a.in, a.in_bytes);
-  const __amdgpu_buffer_rsrc_t rout = make_rsrc(a.out, a.out_bytes);
+  // Resources from the tile's corner of the input (row y0, column x0) and
+  // of the output (row x0, column y0); offsets below are counted from there.
+  const __amdgpu_buffer_rsrc_t rin = rsrc_at(a.in, a.in_bytes, (int64_t)y0 * a.ldi + x0);
+  const __amdgpu_buffer_rsrc_t rout = rsrc_at(a.out, a.out_bytes, (int64_t)x0 * a.ldo + y0);
 
   f32x4 v[LOADS];
 #pragma unroll
@@ -94,7 +97,7 @@ __global__ void __launch_bounds__(256) sgemm_transpose_kernel(TransposeArgs a) {
     const int f = q * 256 + tid;
     const int r = f / UNITS, c = f % UNITS;
     const int gr = y0 + r, gc = x0 + 4 * c;
-    const uint32_t off = ((uint32_t)gr * (uint32_t)a.ldi + (uint32_t)gc) * 4u;
+    const uint32_t off = ((uint32_t)r * (uint32_t)a.ldi + (uint32_t)(4 * c)) * 4u;
     if constexpr (VEC_IN) {
       v[q] = load4(rin, (gr < a.rows && gc < a.cols) ? off : kOob);
     } else {
@@ -123,7 +126,7 @@ __global__ void __launch_bounds__(256) sgemm_transpose_kernel(TransposeArgs a) {
     for (int e = 0; e < 4; ++e) {   // output row x0 + 4 c + e
       const int orow = x0 + 4 * c + e;
       const f32x4 o = {blk[0][e], blk[1][e], blk[2][e], blk[3][e]};
-      const uint32_t off = ((uint32_t)orow * (uint32_t)a.ldo + (uint32_t)ocol) * 4u;
+      const uint32_t off = ((uint32_t)(4 * c + e) * (uint32_t)a.ldo + (uint32_t)(4 * i)) * 4u;
       if constexpr (VEC_OUT) {
         store4(rout, (orow < a.cols && ocol < a.rows) ? off : kOob, o);
       } else {

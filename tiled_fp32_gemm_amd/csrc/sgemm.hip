@@ -18,7 +18,14 @@ namespace {
 
 using sg::GemmArgs;
 
-constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;  // 32-bit offsets, kOob
+// The kernels address each operand from the corner of their own tile with
+// 32-bit byte offsets below 2^31 (kOob = 2^31 marks an element outside the
+// matrix), so what is bounded is one tile's span, not an operand's size.
+constexpr int64_t kMaxSpanBytes = sg::kRsrcMax;
+// Tile origins and sizes are 32-bit ints in the kernels.
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1024;
+// The split partials are addressed as one resource from their first byte.
+constexpr int64_t kMaxWorkspaceBytes = sg::kRsrcMax;
 
 struct Checked {
   int64_t a_bytes = 0, b_bytes = 0, c_bytes = 0;
@@ -59,7 +66,8 @@ int check(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     if (o.p == nullptr || ((uintptr_t)o.p & 3u) != 0) return SGEMM_ERR_INVALID_ARG;
   }
   for (auto& o : ops)
-    if (o.bytes < 0 || o.bytes >= kMaxOperandBytes) return SGEMM_ERR_UNSUPPORTED;
+    if (o.bytes < 0) return SGEMM_ERR_UNSUPPORTED;   // beyond int64
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_ERR_UNSUPPORTED;
   if (overlaps(C, cb, A, ab) || overlaps(C, cb, B, bb)) return SGEMM_ERR_INVALID_ARG;
   out.a_bytes = ab;
   out.b_bytes = bb;
@@ -69,6 +77,35 @@ int check(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// True when rows x width floats with leading dimension ld (the first row
+// starting at offset 0) end below kMaxSpanBytes: ((rows - 1) ld + width) 4
+// bytes, formed without overflow.
+bool span_fits(int64_t rows, int64_t width, int64_t ld) {
+  if (rows <= 0 || width <= 0) return true;
+  const int64_t lim = kMaxSpanBytes / 4;  // floats
+  if (width >= lim) return false;
+  if (rows == 1) return true;
+  if (ld > (lim - 1 - width) / (rows - 1)) return false;
+  return (rows - 1) * ld + width < lim;
+}
+
+// Whether a kernel with BM x BN tiles and BK-deep slabs can address this
+// product: one tile's rows of A (BK columns past a slab's first) and of C,
+// and one slab's rows of B (BN columns past the tile's first), each within
+// kMaxSpanBytes of their first element.  ldc is the leading dimension the
+// tiles are written with (N for the split partials).
+bool tile_fits(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+               int64_t ldc, int bm, int bn, int bk) {
+  if (K > 0 && !span_fits(M < bm ? M : bm, bk, lda)) return false;
+  if (K > 0 && !span_fits(K < bk ? K : bk, bn, ldb)) return false;
+  return span_fits(M < bm ? M : bm, bn, ldc);
+}
+
+// The grid's work-items, workgroups x threads, must fit in 32 bits.
+bool grid_fits(int64_t workgroups, int threads) {
+  return workgroups >= 0 && workgroups < ((int64_t(1) << 32) / threads);
+}
 
 typedef void (*KernelFn)(GemmArgs);
 typedef void (*KernelFnT)(sg::TransposeArgs);
@@ -198,19 +235,31 @@ double estimate(const Candidate& c, int64_t M, int64_t N, int64_t K) {
   return estimate_grid(c, cdiv(M, c.v.tile_m) * cdiv(N, c.v.tile_n), K);
 }
 
-const Candidate& choose_mfma(int64_t M, int64_t N, int64_t K, bool direct) {
+// Whether candidate c can address the product (tile spans, grid size).
+bool candidate_fits(const Candidate& c, int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb, int64_t ldc) {
+  const Variant& v = c.v;
+  return tile_fits(M, N, K, lda, ldb, ldc, v.tile_m, v.tile_n, v.tile_k) &&
+         grid_fits(cdiv(M, v.tile_m) * cdiv(N, v.tile_n), v.threads);
+}
+
+// The candidate with the least estimated time among those that fit; ties
+// keep the earlier (larger-tile) one.  Null when none fits.
+const Candidate* choose_mfma(int64_t M, int64_t N, int64_t K, int64_t lda,
+                             int64_t ldb, int64_t ldc, bool direct) {
   int n;
   const Candidate* c = mfma_candidates(direct, n);
-  int best = 0;
+  const Candidate* best = nullptr;
   double best_t = 0;
   for (int i = 0; i < n; ++i) {
+    if (!candidate_fits(c[i], M, N, K, lda, ldb, ldc)) continue;
     const double t = estimate(c[i], M, N, K);
-    if (i == 0 || t < best_t * 0.995) {
-      best = i;
+    if (best == nullptr || t < best_t * 0.995) {
+      best = &c[i];
       best_t = t;
     }
   }
-  return c[best];
+  return best;
 }
 
 // Split K across workgroups, for grids that leave the chip under-filled:
@@ -232,8 +281,10 @@ struct Choice {
   int splits, k_split;
 };
 
-Choice choose_direct(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
-  Choice best = {&choose_mfma(M, N, K, true), 1, 0};
+Choice choose_direct(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                     int64_t ldc, int64_t ws_bytes) {
+  Choice best = {choose_mfma(M, N, K, lda, ldb, ldc, true), 1, 0};
+  if (best.c == nullptr) return best;
   const double t_one = estimate(*best.c, M, N, K);
   if (ws_bytes <= 0 || M == 0 || N == 0 || K < 2) return best;
   int n;
@@ -249,7 +300,13 @@ Choice choose_direct(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
       const int64_t se = cdiv(K, ks);  // splits actually used
       if (se < 2) continue;
       const int64_t bytes = se * M * N * 4;
-      if (bytes > ws_bytes || bytes >= kMaxOperandBytes) continue;
+      if (bytes > ws_bytes || bytes >= kMaxWorkspaceBytes) continue;
+      // The partial products read A and B as the product does and write
+      // tiles with rows of N floats.
+      if (!tile_fits(M, N, ks, lda, ldb, N, c.v.tile_m, c.v.tile_n, c.v.tile_k) ||
+          !grid_fits(tiles * se, c.v.threads) || !grid_fits(M * cdiv(N, sg::kReduceCols),
+                                                            sg::kReduceThreads))
+        continue;
       const double t = kSplitPartial * estimate_grid(c, tiles * se, ks) + kReduceFixed +
                        (double)(se + 1) * M * N * 4.0 / kReduceBW;
       if (split.splits == 1 || t < t_best) {
@@ -262,8 +319,6 @@ Choice choose_direct(int64_t M, int64_t N, int64_t K, int64_t ws_bytes) {
   return best;
 }
 
-// The candidate with the least estimated time; ties keep the earlier
-// (larger-tile) one.
 KernelFn fma_fn(bool va, bool vb, bool vc) {
   const int idx = (va ? 4 : 0) | (vb ? 2 : 0) | (vc ? 1 : 0);
   static const KernelFn table[8] = {
@@ -312,8 +367,9 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     set_name(p.info, "fma_128x128x16", va, vb);
   } else {
     Choice ch = {nullptr, 1, 0};
-    if (algo == SGEMM_ALGO_MFMA_DIRECT) ch = choose_direct(M, N, K, ws_bytes);
-    else ch.c = &choose_mfma(M, N, K, false);
+    if (algo == SGEMM_ALGO_MFMA_DIRECT) ch = choose_direct(M, N, K, lda, ldb, ldc, ws_bytes);
+    else ch.c = choose_mfma(M, N, K, lda, ldb, ldc, false);
+    if (ch.c == nullptr) return p;  // no tile can address this product
     const Candidate& cand = *ch.c;
     const Variant& v = cand.v;
     p.info.wg_per_cu = cand.occ;
@@ -336,6 +392,12 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
   p.info.workgroups = (M > 0 && N > 0)
                           ? cdiv(M, p.info.tile_m) * cdiv(N, p.info.tile_n) * p.info.splits
                           : 0;
+  // The fixed-tile families (the matrix-core ones were chosen among fitting
+  // candidates above).
+  if (p.info.splits == 1 &&
+      (!tile_fits(M, N, K, lda, ldb, ldc, p.info.tile_m, p.info.tile_n, p.info.tile_k) ||
+       !grid_fits(p.info.workgroups, p.info.threads)))
+    p.fn = nullptr;
   return p;
 }
 
@@ -350,14 +412,15 @@ int launch_gemm(KernelFn fn, int64_t M, int64_t N, int64_t K, const float* A,
   g.A = A;
   g.B = B;
   g.C = C;
-  g.a_bytes = (uint32_t)c.a_bytes;
-  g.b_bytes = (uint32_t)c.b_bytes;
-  g.c_bytes = (uint32_t)c.c_bytes;
+  g.a_bytes = c.a_bytes;
+  g.b_bytes = c.b_bytes;
+  g.c_bytes = c.c_bytes;
   g.M = (int)M;
   g.N = (int)N;
   g.K = (int)K;
-  // A leading dimension only matters past the first row; keep it in range.
-  g.lda = (int)(M > 1 ? lda : (K > 1 ? K : 1));
+  // A leading dimension only matters past the first row of an operand that
+  // is read or written; there the checks bound it below 2^29.
+  g.lda = (int)(M > 1 && K > 0 ? lda : (K > 1 ? K : 1));
   g.ldb = (int)(K > 1 ? ldb : (N > 1 ? N : 1));
   g.ldc = (int)(M > 1 ? ldc : (N > 1 ? N : 1));
   g.tiles_m = (int)cdiv(M, tile_m);
@@ -382,12 +445,12 @@ int launch_reduce(const float* W, int splits, int64_t M, int64_t N, float* C,
   r.W = W;
   r.C = C;
   r.w_bytes = (uint32_t)(splits * M * N * 4);
-  r.c_bytes = (uint32_t)c.c_bytes;
+  r.c_bytes = c.c_bytes;
   r.M = (int)M;
   r.N = (int)N;
   r.ldc = (int)(M > 1 ? ldc : (N > 1 ? N : 1));
   r.splits = splits;
-  r.groups_per_row = (int)cdiv(N, 4);
+  r.chunks = (int)cdiv(N, sg::kReduceCols);
   const bool vw = aligned16(W) && N % 4 == 0;
   const bool vc = vw && aligned16(C) && r.ldc % 4 == 0;
   static const KernelFnR table[3] = {sg::sgemm_split_reduce_kernel<false, false>,
@@ -396,8 +459,8 @@ int launch_reduce(const float* W, int splits, int64_t M, int64_t N, float* C,
   const KernelFnR fn = table[vc ? 2 : (vw ? 1 : 0)];
   void* kargs[] = {&r};
   const hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void*>(fn), dim3((unsigned)cdiv(M * r.groups_per_row, 256)),
-      dim3(256), kargs, 0, stream);
+      reinterpret_cast<const void*>(fn), dim3((unsigned)(M * r.chunks)),
+      dim3(sg::kReduceThreads), kargs, 0, stream);
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
@@ -480,6 +543,10 @@ int sgemm_ladder(int step, int64_t M, int64_t N, int64_t K, const float* A,
   Checked c;
   const int st = check(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_AUTO, c);
   if (st != SGEMM_OK || !c.launch) return st;
+  // Every vector-ALU step walks K in 16-deep slabs.
+  if (!tile_fits(M, N, K, lda, ldb, ldc, ls.tile_m, ls.tile_n, 16) ||
+      !grid_fits(cdiv(M, ls.tile_m) * cdiv(N, ls.tile_n), 256))
+    return SGEMM_ERR_UNSUPPORTED;
   const bool vec = K == 0 || (vec_a_ok(A, lda, K) && vec_b_ok(B, ldb, N));
   return launch_gemm(vec ? ls.vec : ls.sca, M, N, K, A, lda, B, ldb, C, ldc, c,
                      ls.tile_m, ls.tile_n, 256, stream);
@@ -513,9 +580,10 @@ int sgemm_ws(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
 }
 
 int64_t sgemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K < 0) return 0;
-  const Choice ch = choose_direct(M, N, K, kMaxOperandBytes);
-  return ch.splits > 1 ? (int64_t)ch.splits * M * N * 4 : 0;
+  if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  // Contiguous operands (lda = K, ldb = ldc = N).
+  const Choice ch = choose_direct(M, N, K, K > 1 ? K : 1, N, N, kMaxWorkspaceBytes);
+  return ch.c != nullptr && ch.splits > 1 ? (int64_t)ch.splits * M * N * 4 : 0;
 }
 
 int sgemm_plan_query_ws(int64_t M, int64_t N, int64_t K, const float* A,
@@ -525,8 +593,10 @@ int sgemm_plan_query_ws(int64_t M, int64_t N, int64_t K, const float* A,
   Checked c;
   const int st = check(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_AUTO, c);
   if (st != SGEMM_OK) return st;
-  *plan = plan_for(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_MFMA_DIRECT,
-                   workspace_bytes).info;
+  const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_MFMA_DIRECT,
+                          workspace_bytes);
+  if (c.launch && p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;
+  *plan = p.info;
   return SGEMM_OK;
 }
 
@@ -543,7 +613,9 @@ int sgemm_plan_query(int64_t M, int64_t N, int64_t K, const float* A,
   Checked c;
   const int st = check(M, N, K, A, lda, B, ldb, C, ldc, algo, c);
   if (st != SGEMM_OK) return st;
-  *plan = plan_for(M, N, K, A, lda, B, ldb, C, ldc, algo).info;
+  const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, algo);
+  if (c.launch && p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;
+  *plan = p.info;
   return SGEMM_OK;
 }
 
@@ -559,21 +631,28 @@ int sgemm_transpose_ex(int64_t rows, int64_t cols, const float* in,
   const int64_t ib = span_bytes(rows, cols, ldi), ob = span_bytes(cols, rows, ldo);
   if (in == nullptr || out == nullptr || ((uintptr_t)in & 3u) || ((uintptr_t)out & 3u))
     return SGEMM_ERR_INVALID_ARG;
-  if (ib < 0 || ob < 0 || ib >= kMaxOperandBytes || ob >= kMaxOperandBytes)
-    return SGEMM_ERR_UNSUPPORTED;
+  if (ib < 0 || ob < 0) return SGEMM_ERR_UNSUPPORTED;   // beyond int64
   if (overlaps(in, ib, out, ob)) return SGEMM_ERR_INVALID_ARG;
+  // A tile reads rows of the input and writes rows of the output from its
+  // corner with 32-bit offsets.
+  const int64_t tiles = cdiv(cols, sg::kTransposeCols) * cdiv(rows, sg::kTransposeRows);
+  if (rows > kMaxDim || cols > kMaxDim || !grid_fits(tiles, 256) ||
+      !span_fits(rows < sg::kTransposeRows ? rows : sg::kTransposeRows,
+                 sg::kTransposeCols, ldi) ||
+      !span_fits(cols < sg::kTransposeCols ? cols : sg::kTransposeCols,
+                 sg::kTransposeRows, ldo))
+    return SGEMM_ERR_UNSUPPORTED;
 
   sg::TransposeArgs a;
   a.in = in;
   a.out = out;
-  a.in_bytes = (uint32_t)ib;
-  a.out_bytes = (uint32_t)ob;
+  a.in_bytes = ib;
+  a.out_bytes = ob;
   a.rows = (int)rows;
   a.cols = (int)cols;
   a.ldi = (int)(rows > 1 ? ldi : (cols > 1 ? cols : 1));
   a.ldo = (int)(cols > 1 ? ldo : (rows > 1 ? rows : 1));
   a.tiles_x = (int)cdiv(cols, sg::kTransposeCols);
-  const int64_t tiles = cdiv(cols, sg::kTransposeCols) * cdiv(rows, sg::kTransposeRows);
   const bool vi = aligned16(in) && a.ldi % 4 == 0 && cols % 4 == 0;
   const bool vo = aligned16(out) && a.ldo % 4 == 0 && rows % 4 == 0;
   if (layout == SGEMM_TRANSPOSE_AUTO) layout = SGEMM_TRANSPOSE_SWIZZLED;
@@ -603,7 +682,9 @@ const char* sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "success";
     case SGEMM_ERR_INVALID_ARG: return "invalid argument";
-    case SGEMM_ERR_UNSUPPORTED: return "unsupported: an operand spans 2 GiB or more";
+    case SGEMM_ERR_UNSUPPORTED:
+      return "unsupported: a dimension of 2^31 - 1024 or more, one tile's rows of an "
+             "operand spanning 2 GiB or more, or a grid of 2^32 work-items or more";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
