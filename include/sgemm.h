@@ -47,14 +47,16 @@
  *                          unknown algo.
  *   SGEMM_ERR_UNSUPPORTED  M, N or K of 2^31 - 1024 or more; or, for every
  *                          tile the kernel family offers, one tile's rows
- *                          of A or of C, or one K slab's rows of B, would
- *                          span 2 GiB or more (the kernels address an
- *                          operand from the corner of their own tile with
- *                          32-bit byte offsets, so operands themselves may
- *                          be of any size: this needs a leading dimension
- *                          of millions of floats, e.g. lda >= 2^24 with 32
- *                          or more rows of A); or a grid of 2^32 work-items
- *                          or more.  sgemm_plan_query answers the same.
+ *                          of A (all K columns) or of C, or one K slab's
+ *                          rows of B, would span 2 GiB or more (the kernels
+ *                          address an operand from the corner of their own
+ *                          tile with 32-bit byte offsets, so operands
+ *                          themselves may be of any size: this needs a
+ *                          leading dimension of millions of floats, e.g.
+ *                          lda >= 2^24 with 32 or more rows of A, or one
+ *                          row of A of 2^29 floats); or a grid of 2^32
+ *                          work-items or more.  sgemm_plan_query answers
+ *                          the same.
  *   SGEMM_ERR_LAUNCH       the HIP launch reported an error.
  * M == 0 or N == 0 returns SGEMM_OK with nothing enqueued; K == 0 writes
  * C = 0 (the empty sum).

@@ -91,10 +91,12 @@ def test_dimension_limit(lib):
     assert plan(lim + 1, 1, 1)[0] == sg.ERR_UNSUPPORTED
     assert plan(1, lim + 1, 1)[0] == sg.ERR_UNSUPPORTED
     assert plan(1, 1, lim + 1)[0] == sg.ERR_UNSUPPORTED
-    assert plan(1, 1, lim)[0] == sg.OK
-    # M at the limit is allowed, but no tile makes a grid below 2^32
-    # work-items of it
+    # at the limit the other rules decide: M = lim makes no grid below 2^32
+    # work-items, and K = lim puts 8 GiB in one row of A; a row of A just
+    # under 2 GiB is fine
     assert plan(lim, 1, 1)[0] == sg.ERR_UNSUPPORTED
+    assert plan(1, 1, lim)[0] == sg.ERR_UNSUPPORTED
+    assert plan(1, 1, (1 << 29) - 64)[0] == sg.OK
 
 
 def test_grid_limit(lib):
@@ -120,7 +122,7 @@ def test_short_k_with_a_huge_ldb_is_planned(lib):
 
 
 def test_split_workspace_stays_below_2_gib(lib):
-    for M, N, K in ((256, 256, 3 << 20), (1024, 1024, 1 << 20), (64, 64, 1 << 24)):
+    for M, N, K in ((256, 256, 3 << 20), (1024, 1024, 1 << 20), (64, 64, 1 << 22)):
         need = sg.sgemm_workspace_bytes(M, N, K)
         assert 0 < need < 2 * GIB
 

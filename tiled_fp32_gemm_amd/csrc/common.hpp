@@ -6,7 +6,8 @@
 // the tile's first row, C to its first row and column, B to its first column
 // and, slab by slab, to the slab's first row), so that every byte offset a
 // lane forms stays below 2^31 however large the operand is; the host checks
-// that one tile's rows (one slab's rows for B) span less than 2 GiB.  A
+// that one tile's rows of A (over all of K) and of C, and one slab's rows of
+// B, span less than 2 GiB.  A
 // resource is never larger than 2^31 bytes, and a lane whose element lies
 // outside the logical matrix is given the byte offset kOob = 2^31, past its
 // end, so its load returns 0 and its store is dropped by the hardware range
@@ -58,15 +59,36 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                          0, 0);
 }
 
+// min(rem, cap) for a wave-uniform rem >= 0 and cap <= 2^31, formed with
+// 32-bit scalar operations on the two halves: the scalar unit has no 64-bit
+// ordered compare, and a 64-bit one would move the clamp to the vector unit
+// and put a branch in the slab loop.  The empty asm keeps the compiler from
+// folding the halves back into one 64-bit compare.
+__device__ __forceinline__ uint32_t cap_bytes(uint64_t rem, uint32_t cap) {
+  uint32_t hi = (uint32_t)(rem >> 32), lo = (uint32_t)rem;
+  asm volatile("" : "+s"(hi), "+s"(lo));
+  const uint32_t m = lo < cap ? lo : cap;
+  return hi != 0u ? cap : m;
+}
+
 // A resource over an operand of `bytes` bytes starting at `base`, moved
-// `skip` floats forward: the rest of the operand, capped at kRsrcMax bytes
-// (empty when nothing is left).  All arguments are wave-uniform.
+// `skip` floats forward (skip * 4 < bytes): the rest of the operand, capped
+// at kRsrcMax bytes.  All arguments are wave-uniform.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const float* base,
                                                         int64_t bytes,
                                                         int64_t skip) {
-  const int64_t rem = bytes - 4 * skip;
-  const uint32_t n = rem <= 0 ? 0u : (rem >= kRsrcMax ? (uint32_t)kRsrcMax : (uint32_t)rem);
-  return make_rsrc(base + skip, n);
+  return make_rsrc(base + skip, cap_bytes((uint64_t)(bytes - 4 * skip), (uint32_t)kRsrcMax));
+}
+
+// The resource of the K slab starting at column k0 of a tile's rows of A:
+// from base + k0 (base: the tile's first row), cap - 4 k0 bytes, where cap is
+// the capped size of the whole rest of A from base (rsrc_at's size with
+// skip 0).  Exact, and 32-bit only, because the host checks that a tile's
+// rows of A over all of K span less than 2^31 bytes: words below K lie
+// inside it whether or not cap was capped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_slab_a(const float* base,
+                                                            uint32_t cap, int k0) {
+  return make_rsrc(base + k0, cap - 4u * (uint32_t)k0);
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's data lands

@@ -65,7 +65,8 @@ sgemm_fma_kernel(GemmArgs g) {
   // from (m0, n0)); each slab moves A and B on to its own first column and
   // row, so lane offsets are counted from the slab's corner.
   const float* const At = g.A + (int64_t)m0 * g.lda;
-  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const uint32_t a_cap =
+      cap_bytes((uint64_t)(g.a_bytes - 4 * (int64_t)m0 * g.lda), (uint32_t)kRsrcMax);
   const float* const Bt = g.B + n0;
   const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
   const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
@@ -97,7 +98,7 @@ sgemm_fma_kernel(GemmArgs g) {
 
   f32x4 sa[Cfg::A_SLOTS], sb[Cfg::B_SLOTS];
   auto load_slab = [&](int k0) {
-    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_slab_a(At, a_cap, k0);
     const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
 #pragma unroll
     for (int s = 0; s < Cfg::A_SLOTS; ++s) {

@@ -58,14 +58,15 @@ __global__ void __launch_bounds__(256) sgemm_naive_kernel(GemmArgs g) {
   // The tile's corner of A (row m0), B (column n0) and C (m0, n0); A and B
   // move on by 16 values of k at a time.
   const float* const At = g.A + (int64_t)m0 * g.lda;
-  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const uint32_t a_cap =
+      cap_bytes((uint64_t)(g.a_bytes - 4 * (int64_t)m0 * g.lda), (uint32_t)kRsrcMax);
   const float* const Bt = g.B + n0;
   const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
   const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
   const bool row_ok = row < g.M, col_ok = col < g.N;
   float sum = 0.0f;
   for (int k0 = 0; k0 < g.K; k0 += 16) {
-    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_slab_a(At, a_cap, k0);
     const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
     const int kn = min(16, g.K - k0);
     for (int k = 0; k < kn; ++k) {
@@ -127,7 +128,8 @@ sgemm_ladder_kernel(GemmArgs g) {
   // The tile's corner of A (row m0), B (column n0) and C (m0, n0); each
   // slab moves A and B on to its own first column and row.
   const float* const At = g.A + (int64_t)m0 * g.lda;
-  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const uint32_t a_cap =
+      cap_bytes((uint64_t)(g.a_bytes - 4 * (int64_t)m0 * g.lda), (uint32_t)kRsrcMax);
   const float* const Bt = g.B + n0;
   const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
   const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
@@ -145,7 +147,7 @@ sgemm_ladder_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
 
   for (int k0 = 0; k0 < g.K; k0 += BK) {
-    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_slab_a(At, a_cap, k0);
     const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
     // A group f: tile row (f % 16) + 16 (f / 64), k quad (f / 16) % 4.
 #pragma unroll

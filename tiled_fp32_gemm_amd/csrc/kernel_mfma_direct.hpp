@@ -20,8 +20,8 @@
 //   * A groups of rows >= M and B groups starting at a column >= N get the
 //     offset kOob once, and read zeros in every slab;
 //   * B rows k >= K lie past the end of the moved B resource and read zeros
-//     (a row whose offset from the slab's first row would reach 2^31 can
-//     only be such a row, and gets kOob);
+//     (when K is shorter than one slab they get kOob instead, since their
+//     offsets could reach 2^31);
 //   * a B group reaching past column N-1 brings in values that only feed C
 //     columns >= N, which are never stored;
 //   * A words at k >= K of a row below M-1 are inside the allocation (the
@@ -175,7 +175,8 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   // The tile's corner of each operand: A from row m0, B from column n0, C
   // from (m0, n0).  Rows and columns below are counted from there.
   const float* const At = g.A + (int64_t)m0 * g.lda;
-  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const uint32_t a_cap =
+      cap_bytes((uint64_t)(g.a_bytes - 4 * (int64_t)m0 * g.lda), (uint32_t)kRsrcMax);
   const float* const Bt = g.B + n0;
   const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
   const int m_left = g.M - m0, n_left = g.N - n0;
@@ -201,20 +202,19 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   for (int s = 0; s < Cfg::B_SLOTS; ++s) {
     const int u = s * NT + 64 * wave + lane;
     const int k = u / QB, q = (u % QB) ^ ((k & 8) ? 8 : 0);
-    // In floats from the slab's first row, formed in 64 bits: rows past a
-    // short K may lie 2^31 bytes or more away, and must read zeros, not wrap.
-    const uint64_t w = (uint64_t)k * (uint32_t)g.ldb + (uint32_t)(4 * q);
-    b_off[s] = (4 * q < n_left && w < (uint64_t)(kRsrcMax / 4)) ? (uint32_t)w * 4u : kOob;
+    // Rows k < min(K, BK) lie less than 2^31 bytes from a slab's first row
+    // (checked on the host).  With K >= BK that is every row; with K < BK
+    // there is one slab, and its rows past K, which may lie further away,
+    // get kOob rather than an offset that would wrap.
+    b_off[s] = (4 * q < n_left && k < g.K)
+                   ? ((uint32_t)k * (uint32_t)g.ldb + (uint32_t)(4 * q)) * 4u
+                   : kOob;
   }
-  // The resources of the slab starting at k0: A moved by k0 columns, B by
-  // k0 rows, each size shrunk to match; from K on a resource is empty and
-  // reads zeros.
-  auto rsrc_a = [&](int k0) {
-    return k0 < g.K ? rsrc_at(At, a_rem, k0) : make_rsrc(g.A, 0u);
-  };
-  auto rsrc_b = [&](int k0) {
-    return k0 < g.K ? rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb) : make_rsrc(g.B, 0u);
-  };
+  // The resources of the slab starting at k0 (< K: slabs from K on are
+  // never loaded): A moved by k0 columns, B by k0 rows, each size shrunk to
+  // match.
+  auto rsrc_a = [&](int k0) { return rsrc_slab_a(At, a_cap, k0); };
+  auto rsrc_b = [&](int k0) { return rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb); };
 
   // Issue direct load l (the A slots, then the B slots) of a slab with
   // resources (qa, qb) into stage st.
@@ -306,8 +306,10 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   };
   // The matrix instructions of a chunk; with LOADS set, load l of the
   // slab (qa, qb) goes into stage st before k step l * 4 / LOADS.
+  // With pin_first set, the first k step's instructions stay where they are
+  // written; the rest may move (see step).
   auto mfma_chunk = [&](const Frag& f, auto loads, __amdgpu_buffer_rsrc_t qa,
-                        __amdgpu_buffer_rsrc_t qb, int st) {
+                        __amdgpu_buffer_rsrc_t qb, int st, auto pin_first) {
     constexpr bool kLoads = decltype(loads)::value;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
@@ -322,6 +324,8 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
         for (int j = 0; j < TB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][pp], f.b[j][pp],
                                                            acc[i][j], 0, 0, 0);
+      if constexpr (decltype(pin_first)::value)
+        if (pp == 0) __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Chunks 0 .. NCH-2 of slab t (stage st), each after the read of the
@@ -334,7 +338,10 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     for (int c = 0; c + 1 < NCH; ++c) {
       read_chunk(fr[(c + 1) & 1], st, c + 1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk(fr[c & 1], std::false_type(), qz, qz, 0);
+      // With K split over four wave groups, the first k step of the chunk
+      // that precedes the slab barrier stays ahead of it (see step).
+      mfma_chunk(fr[c & 1], std::false_type(), qz, qz, 0,
+                 std::integral_constant<bool, KS == 4>());
     }
   };
   // Slab t (stage st) when a slab t + 1 follows: its chunks, then this
@@ -344,24 +351,40 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   // while (LOADS set) slab t + 2 is loaded into stage st.
   auto step = [&](int t, int st, auto loads) {
     constexpr bool kLoads = decltype(loads)::value;
+    // Slab t + 2's resources are formed here, among slab t's matrix
+    // instructions, rather than between the barrier and the loads.
+    const int k2 = (t + 2) * BK;
+    __amdgpu_buffer_rsrc_t qa = qz, qb = qz;
+    if constexpr (kLoads) {
+      qa = rsrc_a(k2);
+      qb = rsrc_b(k2);
+    }
     chunks(st);
+    // Matrix instructions touch no memory, so the barrier alone does not
+    // keep them ahead of it; where they go was measured on MI355X.  With K
+    // split over two wave groups, every chunk but the last stays ahead of
+    // the barrier (+1 to +5%).  With four groups, whose single accumulator
+    // makes a chunk a chain of dependent instructions, only the chunk's
+    // first k step does (mfma_chunk's pin_first): the matrix pipe has work
+    // across the barrier and the wave still reaches it, and its next loads,
+    // early.  With one group the compiler's own placement measured best.
+    if constexpr (KS == 2) __builtin_amdgcn_sched_barrier(0);
     const int nst = st ^ 1;
     __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
     if (k_tail && t + 2 == nslab) fix_tail(t + 1, nst);
     __builtin_amdgcn_s_waitcnt(kLdsWait);
     asm volatile("s_barrier" ::: "memory");
-    const int k2 = (t + 2) * BK;
     if constexpr (kSpread) {
       read_chunk(fr[0], nst, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk(fr[1], loads, rsrc_a(k2), rsrc_b(k2), st);
+      mfma_chunk(fr[1], loads, qa, qb, st, std::false_type());
     } else {
       // With K split inside the workgroup a wave's chunk is short: its
       // loads go out at once.
-      if constexpr (kLoads) issue(rsrc_a(k2), rsrc_b(k2), st);
+      if constexpr (kLoads) issue(qa, qb, st);
       read_chunk(fr[0], nst, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk(fr[1], std::false_type(), qz, qz, st);
+      mfma_chunk(fr[1], std::false_type(), qz, qz, st, std::false_type());
     }
   };
   if (nslab > 0) {
@@ -379,7 +402,7 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
       ++t;
     }
     chunks(t & 1);
-    mfma_chunk(fr[1], std::false_type(), qz, qz, 0);
+    mfma_chunk(fr[1], std::false_type(), qz, qz, 0, std::false_type());
   }
 
   if constexpr (KS > 1) {

@@ -33,14 +33,15 @@ __global__ void __launch_bounds__(256) sgemm_simple_kernel(GemmArgs g) {
 
   // The tile's corner of A (row m0), B (column n0) and C (m0, n0).
   const float* const At = g.A + (int64_t)m0 * g.lda;
-  const int64_t a_rem = g.a_bytes - 4 * (int64_t)m0 * g.lda;
+  const uint32_t a_cap =
+      cap_bytes((uint64_t)(g.a_bytes - 4 * (int64_t)m0 * g.lda), (uint32_t)kRsrcMax);
   const float* const Bt = g.B + n0;
   const int64_t b_rem = g.b_bytes - 4 * (int64_t)n0;
   const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.C, g.c_bytes, (int64_t)m0 * g.ldc + n0);
 
   float sum = 0.0f;
   for (int k0 = 0; k0 < g.K; k0 += T) {
-    const __amdgpu_buffer_rsrc_t ra = rsrc_at(At, a_rem, k0);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_slab_a(At, a_cap, k0);
     const __amdgpu_buffer_rsrc_t rb = rsrc_at(Bt, b_rem, (int64_t)k0 * g.ldb);
     const bool a_ok = row < g.M && k0 + tx < g.K;
     const bool b_ok = k0 + ty < g.K && col < g.N;

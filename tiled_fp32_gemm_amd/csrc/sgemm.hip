@@ -91,13 +91,13 @@ bool span_fits(int64_t rows, int64_t width, int64_t ld) {
 }
 
 // Whether a kernel with BM x BN tiles and BK-deep slabs can address this
-// product: one tile's rows of A (BK columns past a slab's first) and of C,
-// and one slab's rows of B (BN columns past the tile's first), each within
+// product: one tile's rows of A (all K columns, or BK if more) and of C, and
+// one slab's rows of B (BN columns past the tile's first), each within
 // kMaxSpanBytes of their first element.  ldc is the leading dimension the
 // tiles are written with (N for the split partials).
 bool tile_fits(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                int64_t ldc, int bm, int bn, int bk) {
-  if (K > 0 && !span_fits(M < bm ? M : bm, bk, lda)) return false;
+  if (K > 0 && !span_fits(M < bm ? M : bm, K > bk ? K : bk, lda)) return false;
   if (K > 0 && !span_fits(K < bk ? K : bk, bn, ldb)) return false;
   return span_fits(M < bm ? M : bm, bn, ldc);
 }
