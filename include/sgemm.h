@@ -79,13 +79,14 @@ typedef struct ihipStream_t *hipStream_t;
 extern "C" {
 #endif
 
-#define SGEMM_VERSION 120 /* 1.2.0 */
+#define SGEMM_VERSION 130 /* 1.3.0 */
 
 /* Status codes. */
 #define SGEMM_OK 0
 #define SGEMM_ERR_INVALID_ARG 1
 #define SGEMM_ERR_UNSUPPORTED 2
 #define SGEMM_ERR_LAUNCH 3
+#define SGEMM_ERR_SCRATCH_LIMIT 4   /* sgemm_ws_noalloc only */
 
 /* Kernel families (sgemm_ex).
  *   AUTO    the fastest family, MFMA_DIRECT, with the tile size (and the
@@ -183,6 +184,33 @@ int sgemm_ws(int64_t M, int64_t N, int64_t K,
              const float *B, int64_t ldb,
              float *C, int64_t ldc,
              hipStream_t stream, void *workspace, int64_t workspace_bytes);
+
+/* Bytes of the static scratch sgemm_ws_noalloc splits K into, per device. */
+#define SGEMM_NOALLOC_MAX_BYTES (32 << 20)
+
+/* sgemm_ws for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a file-scope device array of SGEMM_NOALLOC_MAX_BYTES that the
+ * library holds on each device it runs on until the process ends (its
+ * address is looked up once per device, on the first call that splits K on
+ * it); the call itself allocates nothing and frees nothing.
+ *   workspace_bytes  the room the plan may take from the scratch, as
+ *                    sgemm_ws's workspace_bytes (0 allows no split), at most
+ *                    SGEMM_NOALLOC_MAX_BYTES; more is SGEMM_ERR_SCRATCH_LIMIT
+ *                    and a negative value SGEMM_ERR_INVALID_ARG, before any
+ *                    HIP call.
+ * The plan, the kernels and the result are those of sgemm_ws with a
+ * workspace of workspace_bytes, bit for bit.  Every call on a device shares
+ * that device's one scratch, which keeps the last call's partials (each
+ * split call overwrites all it reads): calls that overlap on one device (on
+ * different streams, or from different threads without ordering) race and
+ * must not be made.  Other arguments, checks and return codes are sgemm_ws's;
+ * SGEMM_ERR_LAUNCH also when the scratch's address cannot be had. */
+int sgemm_ws_noalloc(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float *C, int64_t ldc,
+                     hipStream_t stream, int64_t workspace_bytes);
 
 /* The workspace size with which sgemm_ws takes its fastest plan for
  * M x N x K (0 when the best plan does not split K, or for an invalid or

@@ -64,9 +64,10 @@ def test_one_hip_runtime_is_mapped(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert sg.sgemm_version() == 120
+    assert sg.sgemm_version() == 130
     assert sg.sgemm_status_string(sg.OK) == "success"
-    for st in (sg.ERR_INVALID_ARG, sg.ERR_UNSUPPORTED, sg.ERR_LAUNCH):
+    for st in (sg.ERR_INVALID_ARG, sg.ERR_UNSUPPORTED, sg.ERR_LAUNCH,
+               sg.ERR_SCRATCH_LIMIT):
         assert sg.sgemm_status_string(st) not in ("", "success")
     assert sg.sgemm_status_string(12345) == "unknown status"
 

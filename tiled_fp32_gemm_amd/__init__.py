@@ -1,6 +1,6 @@
 """Python binding of the gfx950 SGEMM library (``include/sgemm.h``).
 
-The functions ``sgemm``, ``sgemm_ex``, ``sgemm_ws``,
+The functions ``sgemm``, ``sgemm_ex``, ``sgemm_ws``, ``sgemm_ws_noalloc``,
 ``sgemm_workspace_bytes``, ``sgemm_plan_query``, ``sgemm_plan_query_ws``,
 ``sgemm_transpose``, ``sgemm_transpose_ex``, ``sgemm_ladder*``,
 ``sgemm_status_string`` and ``sgemm_version`` have the C names and arguments
@@ -29,15 +29,18 @@ __all__ = ["sgemm", "sgemm_ex", "sgemm_plan_query", "sgemm_status_string",
            "sgemm_transpose_ex", "transpose", "TRANSPOSE_LAYOUTS",
            "sgemm_ladder", "sgemm_ladder_steps", "sgemm_ladder_name",
            "ladder_steps", "sgemm_ws", "sgemm_workspace_bytes",
-           "sgemm_plan_query_ws"]
+           "sgemm_plan_query_ws", "sgemm_ws_noalloc", "ERR_SCRATCH_LIMIT",
+           "NOALLOC_MAX_BYTES"]
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+NOALLOC_MAX_BYTES = 32 << 20   # SGEMM_NOALLOC_MAX_BYTES
 ALGOS = {"auto": 0, "simple": 1, "fma": 2, "mfma": 3, "mfma_direct": 4}
 EXPORTED_SYMBOLS = ("sgemm", "sgemm_ex", "sgemm_plan_query",
                     "sgemm_transpose", "sgemm_transpose_ex",
                     "sgemm_status_string", "sgemm_version",
                     "sgemm_ladder_steps", "sgemm_ladder_name", "sgemm_ladder",
-                    "sgemm_ws", "sgemm_workspace_bytes", "sgemm_plan_query_ws")
+                    "sgemm_ws", "sgemm_workspace_bytes", "sgemm_plan_query_ws",
+                    "sgemm_ws_noalloc")
 TRANSPOSE_LAYOUTS = {"auto": 0, "naive": 1, "padded": 2, "swizzled": 3}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +110,8 @@ def load():
     lib.sgemm_ladder.restype = i32
     lib.sgemm_ws.argtypes = common + [fp, fp, i64]
     lib.sgemm_ws.restype = i32
+    lib.sgemm_ws_noalloc.argtypes = common + [fp, i64]
+    lib.sgemm_ws_noalloc.restype = i32
     lib.sgemm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.sgemm_workspace_bytes.restype = i64
     lib.sgemm_plan_query_ws.argtypes = common + [i64, ctypes.POINTER(SgemmPlan)]
@@ -138,6 +143,13 @@ def sgemm_ws(M, N, K, A, lda, B, ldb, C, ldc, stream=0, workspace=0,
     """``sgemm`` that may split K across workgroups into ``workspace``."""
     return load().sgemm_ws(M, N, K, A, lda, B, ldb, C, ldc, stream, workspace,
                            workspace_bytes)
+
+
+def sgemm_ws_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=0,
+                     workspace_bytes=0) -> int:
+    """``sgemm_ws`` over the library's static scratch (no allocation)."""
+    return load().sgemm_ws_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                                   workspace_bytes)
 
 
 def sgemm_workspace_bytes(M, N, K) -> int:

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sgemm.h"
 #include "kernel_fma.hpp"
 #include "kernel_ladder.hpp"
@@ -464,6 +466,38 @@ int launch_reduce(const float* W, int splits, int64_t M, int64_t N, float* C,
   return e == hipSuccess ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
+// The workspace of sgemm_ws_noalloc: a file-scope device array, of which
+// every device the library runs on holds its own copy (at its own address)
+// until the process ends.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress; the kernels get the device address from scratch_of.
+constexpr int64_t kScratchBytes = SGEMM_NOALLOC_MAX_BYTES;
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  float* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of device dev's scratch, looked up once per device
+// (dev must be the current device); null when HIP reports an error.
+float* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+      slot.ptr = static_cast<float*>(p);
+  });
+  return slot.ptr;
+}
+
 // The ablation ladder.  Each step changes one thing against the one before;
 // the vector-ALU steps 0-10 run the kernels of kernel_ladder.hpp (and the
 // pages' basic tiled loop, kernel_simple.hpp), the last three the product
@@ -568,6 +602,35 @@ int sgemm_ws(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
     return launch_gemm(p.fn, M, N, K, A, lda, B, ldb, C, ldc, c, p.info.tile_m,
                        p.info.tile_n, p.info.threads, stream);
   float* W = static_cast<float*>(workspace);
+  const int64_t wb = p.info.workspace_bytes;
+  if (overlaps(W, wb, A, c.a_bytes) || overlaps(W, wb, B, c.b_bytes) ||
+      overlaps(W, wb, C, c.c_bytes))
+    return SGEMM_ERR_INVALID_ARG;
+  const int e = launch_gemm(p.fn, M, N, K, A, lda, B, ldb, W, N, c, p.info.tile_m,
+                            p.info.tile_n, p.info.threads, stream, p.info.splits,
+                            p.k_split, W);
+  if (e != SGEMM_OK) return e;
+  return launch_reduce(W, p.info.splits, M, N, C, ldc, c, stream);
+}
+
+int sgemm_ws_noalloc(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                     const float* B, int64_t ldb, float* C, int64_t ldc,
+                     hipStream_t stream, int64_t workspace_bytes) {
+  if (workspace_bytes < 0) return SGEMM_ERR_INVALID_ARG;
+  if (workspace_bytes > kScratchBytes) return SGEMM_ERR_SCRATCH_LIMIT;
+  Checked c;
+  const int st = check(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_AUTO, c);
+  if (st != SGEMM_OK || !c.launch) return st;
+  const Plan p = plan_for(M, N, K, A, lda, B, ldb, C, ldc, SGEMM_ALGO_MFMA_DIRECT,
+                          workspace_bytes);
+  if (p.fn == nullptr) return SGEMM_ERR_UNSUPPORTED;
+  if (p.info.splits == 1)
+    return launch_gemm(p.fn, M, N, K, A, lda, B, ldb, C, ldc, c, p.info.tile_m,
+                       p.info.tile_n, p.info.threads, stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SGEMM_ERR_LAUNCH;
+  float* const W = scratch_of(dev);
+  if (W == nullptr) return SGEMM_ERR_LAUNCH;
   const int64_t wb = p.info.workspace_bytes;
   if (overlaps(W, wb, A, c.a_bytes) || overlaps(W, wb, B, c.b_bytes) ||
       overlaps(W, wb, C, c.c_bytes))
@@ -686,6 +749,8 @@ const char* sgemm_status_string(int status) {
       return "unsupported: a dimension of 2^31 - 1024 or more, one tile's rows of an "
              "operand spanning 2 GiB or more, or a grid of 2^32 work-items or more";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
+    case SGEMM_ERR_SCRATCH_LIMIT:
+      return "workspace request beyond the 32 MiB static scratch of sgemm_ws_noalloc";
     default: return "unknown status";
   }
 }
