@@ -407,7 +407,8 @@ def bench_ws(args) -> int:
                                f"K={K}, row-major fp32, A,B {dist} seed {seed}",
                    "M": M, "N": N, "K": K, "kernel": plan.kernel.decode(),
                    "splits": plan.splits, "workspace_bytes": plan.workspace_bytes,
-                   "workgroups": plan.workgroups,
+                   "workgroups": plan.workgroups, "threads": plan.threads,
+                   "device": torch.cuda.get_device_name(dev),
                    "event_timed_launches": len(ev_ms),
                    "call_ms_median": round(float(np.median(ev_ms)), 5),
                    "sgemm_same_shape_tflops": round(flops * args.steps / wall_p / 1e12, 3),

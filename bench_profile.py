@@ -108,11 +108,13 @@ def read_csv(out: str, kind: str) -> list:
         return list(csv.DictReader(f))
 
 
-def counters(out: str) -> dict:
-    """{(kernel name, counter): [value per dispatch]}"""
+def counters(out: str, grid=None) -> dict:
+    """{(kernel name, counter): [value per dispatch]}, of the dispatches of
+    `grid` work-items only when given."""
     agg = collections.defaultdict(list)
     for r in read_csv(out, "counter_collection"):
-        agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        if grid is None or int(r["Grid_Size"]) == grid:
+            agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
     return agg
 
 
@@ -124,9 +126,11 @@ def per_dispatch(agg: dict, kernel: str, counter: str) -> tuple:
     return sum(xs) / len(xs), min(xs), max(xs), len(xs)
 
 
-def durations(out: str, kernel: str) -> list:
-    """Dispatch durations (ns) of kernel, in dispatch order."""
-    rows = [r for r in read_csv(out, "kernel_trace") if r["Kernel_Name"].startswith(kernel)]
+def durations(out: str, kernel: str, grid=None) -> list:
+    """Dispatch durations (ns) of kernel (of `grid` work-items only, when
+    given), in dispatch order."""
+    rows = [r for r in read_csv(out, "kernel_trace") if r["Kernel_Name"].startswith(kernel)
+            and (grid is None or int(r["Grid_Size_X"]) == grid)]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
 
@@ -161,13 +165,14 @@ def copy_scale(raw: str) -> tuple:
     return _copy_scale
 
 
-def traffic_pass(raw: str, tag: str, bench_args: list) -> tuple:
-    """({kernel: (fetch KiB, write KiB, dispatches)}, commands) per dispatch."""
+def traffic_pass(raw: str, tag: str, bench_args: list, grid=None) -> tuple:
+    """({kernel: {counter: (KiB per dispatch, dispatches)}}, commands), of
+    the dispatches of `grid` work-items only when given."""
     res, shown = {}, []
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         out, _, cmd = rocprof(raw, f"{tag}_{c}", ["--pmc", c], bench_args, 180)
         shown.append(cmd)
-        for (k, cc), v in counters(out).items():
+        for (k, cc), v in counters(out, grid).items():
             if cc == c:
                 res.setdefault(k, {})[c] = (sum(v) / len(v), len(v))
     return res, shown
@@ -294,42 +299,60 @@ def profile_split(workload: str, raw: str, dest: str) -> list:
     M, N, K, S = cfg["M"], cfg["N"], cfg["K"], cfg["splits"]
     flops = 2.0 * M * N * K
     fn = "sgemm_mfma_direct_kernel"
-    dur = durations(out, fn)
-    red = durations(out, REDUCE_KERNEL)
     steps = b["steps"]
-    # timed region: steps of (split, reduce), then steps of plain sgemm
-    plain = dur[-steps:]
-    split_part = dur[:-steps][-steps:]
-    red_t = red[-steps:]
+    # The split kernel and plain sgemm share the kernel's name; their grids
+    # tell them apart (the split grid is S times the plain one).
+    split_grid = cfg["workgroups"] * cfg["threads"]
+    split_part = durations(out, fn, split_grid)[-steps:]
+    rows = [r for r in read_csv(out, "kernel_trace") if r["Kernel_Name"].startswith(fn)
+            and int(r["Grid_Size_X"]) != split_grid]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    plain = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows][-steps:]
+    plain_grid = int(rows[-1]["Grid_Size_X"])
+    plain_wgs = plain_grid // int(rows[-1]["Workgroup_Size_X"])
+    red_t = durations(out, REDUCE_KERNEL)[-steps:]
     avg = lambda xs: sum(xs) / len(xs)
     short = args + ["--steps", "5", "--warmup", "1", "--warmup-seconds", "0"]
-    res, cmds = traffic_pass(raw, f"traffic_ws_{workload}", short)
     fs, ws, _ = copy_scale(raw)
-    # with --pmc the dispatches of one kernel name are pooled: the split kernel's
-    # partial-product dispatches and plain sgemm's share sgemm_mfma_direct_kernel
-    rk = kib(res, REDUCE_KERNEL, "FETCH_SIZE")[0], kib(res, REDUCE_KERNEL, "WRITE_SIZE")[0]
+    res_s, cmds = traffic_pass(raw, f"traffic_ws_{workload}", short, split_grid)
+    res_p, _ = traffic_pass(raw, f"traffic_ws_plain_{workload}", short, plain_grid)
+    res_r, _ = traffic_pass(raw, f"traffic_ws_reduce_{workload}", short)
+
+    def hbm(res, kernel):
+        f, w = kib(res, kernel, "FETCH_SIZE")[0], kib(res, kernel, "WRITE_SIZE")[0]
+        return (f * fs + w * ws) * 1024, f, w
+
+    hs, hp, hr = hbm(res_s, fn), hbm(res_p, fn), hbm(res_r, REDUCE_KERNEL)
+    call = avg(split_part) + avg(red_t)
     lines = [f"# K split across workgroups (sgemm_ws): {cfg['kernel']}, M={M} N={N} K={K}, "
              f"{S} splits", made,
              f"command_trace: {cmd_t}",
-             f"command_counters: {cmds[0]}   (then WRITE_SIZE; scale factors from the 256 MiB "
-             f"copy calibration: fetch {fs:.4f}, write {ws:.4f})",
-             f"device: {cfg.get('device')}, 1 GPU", "",
+             f"command_counters: {cmds[0]}   (then WRITE_SIZE, each in a run of its own; "
+             f"scale factors from the 256 MiB copy calibration: fetch {fs:.4f}, write "
+             f"{ws:.4f}); the split kernel's dispatches ({split_grid} work-items) and plain "
+             f"sgemm's ({plain_grid}) are told apart by their grids",
+             f"device: {cfg.get('device')}, 1 GPU; source_hash: {cfg.get('source_hash')}", "",
              f"per kernel, trace average over the {steps} timed dispatches:",
              f"  partial products (split kernel): {fn}, {cfg['workgroups']} workgroups",
              f"    average_ns: {avg(split_part):.0f}",
              f"    tflops: {flops / avg(split_part) / 1e3:.2f}",
+             f"    hbm_bytes_per_launch: {hs[0]:.0f}   (fetch {hs[1]:.1f} KiB, write "
+             f"{hs[2]:.1f} KiB per dispatch)",
+             f"    algorithmic_bytes_per_launch: {4 * (M * K + K * N + S * M * N)}",
              f"  fixed-order sum (reduce kernel): {REDUCE_KERNEL}",
              f"    average_ns: {avg(red_t):.0f}",
-             f"    hbm_bytes_per_launch: {(rk[0] * fs + rk[1] * ws) * 1024:.0f}   "
-             f"(fetch {rk[0]:.1f} KiB, write {rk[1]:.1f} KiB per dispatch)",
+             f"    hbm_bytes_per_launch: {hr[0]:.0f}   (fetch {hr[1]:.1f} KiB, write "
+             f"{hr[2]:.1f} KiB per dispatch)",
              f"    algorithmic_bytes_per_launch: {(S + 1) * M * N * 4}",
              f"    gbs_algorithmic: {(S + 1) * M * N * 4 / avg(red_t):.1f}",
-             f"  plain sgemm, same shape: {fn}",
+             f"  plain sgemm, same shape: {fn}, {plain_wgs} workgroups",
              f"    average_ns: {avg(plain):.0f}",
-             f"    tflops: {flops / avg(plain) / 1e3:.2f}", "",
-             f"split call = partial + sum kernels: {avg(split_part) + avg(red_t):.0f} ns -> "
-             f"{flops / (avg(split_part) + avg(red_t)) / 1e3:.2f} TFLOP/s; plain sgemm "
-             f"{avg(plain):.0f} ns -> gain {avg(plain) / (avg(split_part) + avg(red_t)):.2f}x",
+             f"    tflops: {flops / avg(plain) / 1e3:.2f}",
+             f"    hbm_bytes_per_launch: {hp[0]:.0f}",
+             f"    algorithmic_bytes_per_launch: {4 * (M * K + K * N + M * N)}", "",
+             f"split call = partial + sum kernels: {call:.0f} ns -> "
+             f"{flops / call / 1e3:.2f} TFLOP/s; plain sgemm {avg(plain):.0f} ns -> gain "
+             f"{avg(plain) / call:.2f}x",
              "", "bench.py line of the same run:",
              f"  value_tflops: {b['value']}",
              f"  roofline_achieved_tflops: {b['roofline']['achieved']}",
