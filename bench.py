@@ -45,6 +45,12 @@ workspace of ``sgemm_workspace_bytes``) on the workload, with the plain
 hipBLASLt) side by side on a fixed list of shapes, as context: one JSON line
 per shape, both under the same warm-up and operand rotation.
 
+``--op kscan`` runs the product on the workload's M x N for each K of
+``--ks`` (0 included: C = 0, the launch and the stores alone), --steps
+launches each, one JSON line per K with the plan and the event-timed median:
+with a kernel trace over it (bench_profile.py kscan) it separates a launch's
+fixed cost from its cost per K slab.
+
 ``--copy-calibration`` instead runs a device-to-device copy of known size (for
 the counter scale factors) and prints its size.  ``--op transpose`` measures
 the tiled transpose instead (``--layout``; HBM-bound, GB/s against 8 TB/s,
@@ -571,6 +577,46 @@ def bench_ladder(args) -> int:
     return 0
 
 
+def bench_kscan(args) -> int:
+    """The product kernel on the workload's M x N at each K of --ks."""
+    import numpy as np
+    import torch
+
+    import seedgen
+    import tiled_fp32_gemm_amd as sg
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sg.load()
+    M, N, K0, dist, seed = WORKLOADS[args.workload]
+    # By default K0 +- multiples of 32 (same partial last slab, so the planner
+    # keeps the workload's tile), and 0.
+    ks = [int(k) for k in args.ks.split(",")] if args.ks else sorted(
+        {0} | {k for k in (K0 + 32 * j for j in range(-64, 48, 4)) if 0 < k <= 2 * K0 + 512})
+    kmax = max(max(ks), 1)
+    A, B = seedgen.gemm_inputs(M, N, kmax, dist, seed)
+    dev = torch.device("cuda:0")
+    tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    tC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for K in ks:
+        def step():
+            st = sg.sgemm(M, N, K, tA.data_ptr(), kmax, tB.data_ptr(), N, tC.data_ptr(), N,
+                          stream.cuda_stream)
+            if st != sg.OK:
+                raise sg.SgemmError(st, "sgemm")
+        wall, ev_ms, warm = timed_steps(step, args, stream)
+        st, plan = sg.sgemm_plan_query(M, N, K, tA.data_ptr(), kmax, tB.data_ptr(), N,
+                                       tC.data_ptr(), N, 0)
+        print(json.dumps({"metric": "kscan", "M": M, "N": N, "K": K,
+                          "kernel": plan.kernel.decode(), "tile_k": plan.tile_k,
+                          "workgroups": plan.workgroups, "steps": args.steps,
+                          "warmup": warm[0], "clock_ramp_launches": warm[2],
+                          "event_ms_median": round(float(np.median(ev_ms)), 5)}),
+              flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -595,7 +641,10 @@ def main() -> int:
     ap.add_argument("--shapes", default=None,
                     help="--op vendor: comma-separated MxNxK list instead of the built-in one")
     ap.add_argument("--op", default="sgemm",
-                    choices=["sgemm", "sgemm_ws", "transpose", "vendor"])
+                    choices=["sgemm", "sgemm_ws", "transpose", "vendor", "kscan"])
+    ap.add_argument("--ks", default=None,
+                    help="--op kscan: comma-separated K values (default: 0 to 2048 "
+                         "around the workload's K)")
     ap.add_argument("--ladder", action="store_true",
                     help="run every ablation ladder step on the workload")
     ap.add_argument("--layout", default="auto",
@@ -629,6 +678,8 @@ def main() -> int:
         return bench_ws(args)
     if args.op == "vendor":
         return bench_vendor(args)
+    if args.op == "kscan":
+        return bench_kscan(args)
     if args.ladder:
         return bench_ladder(args)
 

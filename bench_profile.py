@@ -19,6 +19,7 @@ factor each counter reads on a plain 256 MiB device copy.
   python3 bench_profile.py split --workload 256x256x8192    split_<kernel>_<workload>.txt
   python3 bench_profile.py ladder                     ladder_4096cube.txt
   python3 bench_profile.py transpose                  transpose_layouts_8192x8192.txt
+  python3 bench_profile.py kscan --workload ragged     kscan_<kernel>_<workload>.txt
   python3 bench_profile.py all                        all of the above, every workload
 
 --out sets where the summaries go (default: profiles/ of this checkout),
@@ -461,6 +462,69 @@ def profile_transpose(raw: str, dest: str) -> list:
     return [_write(dest, f"transpose_layouts_{rows}x{cols}.txt", lines)]
 
 
+def profile_kscan(workload: str, raw: str, dest: str) -> list:
+    """Trace durations of the product kernel over K at the workload's M x N:
+    the fixed cost of a launch (K = 0: the launch and the C stores) and the
+    cost per K slab (a least-squares line over the K of the workload's own
+    plan), against the slab's compute at the matrix peak."""
+    made = header_cmd(f"kscan --workload {workload}")
+    args = ["--op", "kscan", "--workload", workload, "--steps", "50", "--warmup", "5"]
+    out, stdout, cmd = rocprof(raw, f"kscan_{workload}", ["--kernel-trace"], args, 600)
+    lines_b = bench_lines(stdout)
+    rows = [r for r in read_csv(out, "kernel_trace") if "sgemm" in r["Kernel_Name"]
+            and "probe" not in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    table, pos, pts = [], 0, []
+    M, N = lines_b[0]["M"], lines_b[0]["N"]
+    import bench
+    K0 = bench.WORKLOADS[workload][2]
+    plan0 = [d for d in lines_b if d["K"] == K0][0]["kernel"]
+    for d in lines_b:
+        n = d["clock_ramp_launches"] + d["warmup"] + d["steps"]
+        seg = rows[pos:pos + n][-d["steps"]:]
+        pos += n
+        dur = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in seg)
+        med = dur[len(dur) // 2] / 1e3
+        slabs = -(-d["K"] // d["tile_k"]) if d["K"] else 0
+        table.append(f"  K={d['K']:6d}  slabs={slabs:4d}  trace_median_us={med:9.3f}  "
+                     f"kernel={d['kernel']}")
+        if d["kernel"][:-5] == plan0[:-5] and d["K"] > 0:   # any load form
+            pts.append((slabs, med))
+    if pos != len(rows):
+        raise RuntimeError(f"kscan: {len(rows)} dispatches, expected {pos}")
+    n = len(pts)
+    sx, sy = sum(p[0] for p in pts), sum(p[1] for p in pts)
+    sxx, sxy = sum(p[0] ** 2 for p in pts), sum(p[0] * p[1] for p in pts)
+    slope = (n * sxy - sx * sy) / (n * sxx - sx * sx)
+    icpt = (sy - slope * sx) / n
+    wl = [d for d in lines_b if d["K"] == K0][0]
+    tk, wgs = wl["tile_k"], wl["workgroups"]
+    m = plan0.split("_")[2].split("x")
+    bm, bn = int(m[0]), int(m[1])
+    per_cu = -(-wgs // 256)   # tiles per CU
+    slab_peak_us = per_cu * 2.0 * bm * bn * tk / (157.3e12 / 256) * 1e6
+    slabs0 = -(-K0 // tk)
+    floor = [d for d in lines_b if d["K"] == 0]
+    k0_us = None
+    if floor:
+        i0 = lines_b.index(floor[0])
+        k0_us = float(table[i0].split("trace_median_us=")[1].split()[0])
+    lines = [f"# Launch cost against K: {plan0}, M={M} N={N} (workload {workload}, "
+             f"K={K0}), MI355X", made, f"command: {cmd}", "",
+             "per K (trace median of the 50 timed launches):", *table, "",
+             f"fit over the {n} points with the workload's kernel: duration = "
+             f"{icpt:.3f} us + {slope:.4f} us x slabs",
+             f"slab at the FP32 matrix peak: {per_cu} tiles per CU x 2 x {bm} x {bn} x {tk} "
+             f"flop / 614.5 GFLOP/s = {slab_peak_us:.4f} us -> steady slabs run at "
+             f"{slab_peak_us / slope:.3f} of peak",
+             f"K = 0 (launch + C stores only): {k0_us} us",
+             f"workload: {slabs0} slabs -> fit {icpt + slope * slabs0:.3f} us; at the peak "
+             f"per slab with the measured fixed cost: {icpt + slab_peak_us * slabs0:.3f} us "
+             f"= {2.0 * M * N * K0 / ((icpt + slab_peak_us * slabs0) * 1e-6) / 1e12:.1f} "
+             f"TFLOP/s"]
+    return [_write(dest, f"kscan_{plan0}_{workload}.txt", lines)]
+
+
 def lds_conflicts(workload: str, raw: str) -> tuple:
     """(plan name, SQ_LDS_BANK_CONFLICT per dispatch of the product kernel)
     for a short bench run of the workload: the pages' bank-conflict reading
@@ -489,7 +553,7 @@ def _write(dest: str, name: str, lines: list) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("what", choices=["gemm", "split", "ladder", "transpose", "all"])
+    ap.add_argument("what", choices=["gemm", "split", "ladder", "transpose", "kscan", "all"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
@@ -506,6 +570,9 @@ def main() -> int:
         done += profile_ladder(raw, dest)
     if args.what in ("transpose", "all"):
         done += profile_transpose(raw, dest)
+    if args.what in ("kscan", "all"):
+        for w in [args.workload] if args.workload and args.what == "kscan" else ["ragged"]:
+            done += profile_kscan(w, raw, dest)
     say(f"{len(done)} summaries written")
     return 0
 

@@ -114,7 +114,8 @@ DIRECT = [("Li256ELi256ELi64ELi64ELi32ELi1E", 2, 2, 2),
 @pytest.mark.parametrize("frag,ta,tb,subs", DIRECT, ids=[d[0] for d in DIRECT])
 def test_direct_kernel_lds_traffic(asm, frag, ta, tb, subs, split):
     # the same main loop with and without K split across workgroups
-    c = counts(main_loop(kernel_body(asm, "sgemm_mfma_direct_kernel", frag + split)))
+    # (two LDS stages: the Li2E before the split flag)
+    c = counts(main_loop(kernel_body(asm, "sgemm_mfma_direct_kernel", frag + "Li2E" + split)))
     assert not c["other_reads"]
     # per 16-deep sub-slab: 8 steps of TA x TB matrix instructions, fed by
     # two 128-bit A reads per 32-row block and eight B words per 32 columns

@@ -60,8 +60,10 @@ def matching(kernels, plan):
     name = plan.kernel.decode()
     if name.startswith("mfma_lds_"):
         ks = int(re.search(r"_ks(\d+)", name).group(1)) if "_ks" in name else 1
+        stages = int(re.search(r"_s(\d+)", name).group(1)) if re.search(r"_s\d", name) else 2
         want = lambda s, a: ("direct_kernel" in s and a[0] == plan.tile_m and
-                             a[1] == plan.tile_n and a[4] == plan.tile_k and a[5] == ks)
+                             a[1] == plan.tile_n and a[4] == plan.tile_k and a[5] == ks and
+                             a[6] == stages)
     elif name.startswith("mfma_"):
         want = lambda s, a: ("17sgemm_mfma_kernel" in s and a[0] == plan.tile_m and
                              a[1] == plan.tile_n and a[4] == plan.tile_k)

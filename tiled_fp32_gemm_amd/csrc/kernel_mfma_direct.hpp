@@ -53,7 +53,10 @@
 //     alternatives to padding, applied at 16-byte granularity so that the
 //     128-bit units stay whole).
 //
-// Pipeline.  Slabs alternate between the two stages.  A wave reads its MFMA
+// Pipeline.  Slabs rotate through STAGES LDS stages (two for the large tiles,
+// whose stages fill the LDS; four for small tiles, whose slabs compute too
+// briefly to cover a load's latency with one slab in flight), so that
+// STAGES - 1 slabs are in flight.  A wave reads its MFMA
 // fragments one 8-deep chunk ahead of the matrix instructions that use them,
 // into two register sets of one chunk each (the registers one 16-deep
 // sub-slab would take), and the slab barrier sits before the last chunk's
@@ -86,10 +89,10 @@
 
 namespace sg {
 
-template <int BM, int BN, int WM, int WN, int BK_ = 32, int KS_ = 1>
+template <int BM, int BN, int WM, int WN, int BK_ = 32, int KS_ = 1, int STAGES_ = 2>
 struct DirectCfg {
   static constexpr int BK = BK_, KS = KS_;
-  static constexpr int STAGES = 2;          // slab buffers in LDS
+  static constexpr int STAGES = STAGES_;    // slab buffers in LDS
   static constexpr int SUB = BK / 16;       // 16-deep sub-slabs per slab
   static constexpr int SUB_G = SUB / KS;    // ... per wave group
   static constexpr int CPR = BK / 4;        // 16-byte k groups per A row
@@ -112,6 +115,7 @@ struct DirectCfg {
   static_assert(LOADS < 64, "wait count must fit the 6-bit field");
   static_assert(BK % 16 == 0, "slabs of whole sub-slabs");
   static_assert(SUB % KS == 0, "each wave group takes whole sub-slabs");
+  static_assert(STAGES >= 2 && (STAGES - 2) * LOADS < 64, "stages");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -127,18 +131,20 @@ struct VmWait {
 // 0, the other counts at their maxima).
 constexpr int kLdsWait = 0xF | (0x7 << 4) | (0x3 << 14);
 
-template <int BM, int BN, int WM, int WN, int BK_ = 32, int KS_ = 1, bool SPLIT = false>
+template <int BM, int BN, int WM, int WN, int BK_ = 32, int KS_ = 1, int STAGES_ = 2,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(64 * (BM / WM) * (BN / WN) * KS_)
 sgemm_mfma_direct_kernel(GemmArgs g_in) {
-  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, KS_>;
+  using Cfg = DirectCfg<BM, BN, WM, WN, BK_, KS_, STAGES_>;
+  constexpr int S = Cfg::STAGES;
   constexpr int BK = Cfg::BK, NT = Cfg::NT, TA = Cfg::TA, TB = Cfg::TB;
   constexpr int CPR = Cfg::CPR;
   constexpr int KS = Cfg::KS, SUB_G = Cfg::SUB_G;
   constexpr int QB = BN / 4;  // 16-byte units per B row
 
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS_FLOATS];
-  float* const As = lds;                                // [2][A_STAGE]
-  float* const Bs = lds + Cfg::STAGES * Cfg::A_STAGE;   // [2][B_STAGE]
+  float* const As = lds;                                // [STAGES][A_STAGE]
+  float* const Bs = lds + Cfg::STAGES * Cfg::A_STAGE;   // [STAGES][B_STAGE]
 
   // Split K across workgroups: this workgroup's K range becomes the whole
   // product of a narrower A and a shorter B, its tile goes to the partial
@@ -249,9 +255,11 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   const bool k_tail = g.K % BK != 0;  // the last slab reaches past k = K
 
   // Zeroes this lane's own A words at k >= K of slab t in stage st, once its
-  // loads have landed (rows >= M read zeros already).  Runs once per tile:
-  // the lane's unit is worked out again here rather than kept in registers
-  // through the loop.
+  // loads have landed (rows >= M read zeros already): each 16-byte unit that
+  // reaches past K is read and written back whole, so that the 16 lanes an
+  // LDS access serves together (16 rows of one k group, 16 consecutive
+  // units) touch every bank once.  Runs once per tile: the lane's unit is
+  // worked out again here rather than kept in registers through the loop.
   auto fix_tail = [&](int t, int st) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -261,10 +269,13 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
       a_unit(s, ln, row, c);
       const int k = t * BK + 4 * c;
       if (k + 4 > g.K && row < m_left) {
-        float* unit = As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + ln);
+        f32x4* unit =
+            reinterpret_cast<f32x4*>(As + st * Cfg::A_STAGE + 4 * (s * NT + 64 * wave + ln));
+        f32x4 v = *unit;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (k + e >= g.K) unit[e] = 0.0f;
+          if (k + e >= g.K) v[e] = 0.0f;
+        *unit = v;
       }
     }
   };
@@ -344,20 +355,23 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
                  std::integral_constant<bool, KS == 4>());
     }
   };
-  // Slab t (stage st) when a slab t + 1 follows: its chunks, then this
-  // wave's loads of slab t + 1 and its reads of the last chunk are waited
-  // for, the barrier publishes slab t + 1 and frees stage st, the first
-  // chunk of slab t + 1 is read, and the last chunk of slab t computes
-  // while (LOADS set) slab t + 2 is loaded into stage st.
+  // Slab t (stage st = t mod S; slab j always lives in stage j mod S) when
+  // a slab t + 1 follows: its chunks, then this wave's loads of slab t + 1
+  // and its reads of the last chunk are waited for, the barrier publishes
+  // slab t + 1 and frees stage st, the first chunk of slab t + 1 is read,
+  // and the last chunk of slab t computes while (LOADS set) slab t + S is
+  // loaded into stage st.  With LOADS set, slabs t + 2 .. t + S - 1 are in
+  // flight behind slab t + 1 and stay so across the wait; without, the
+  // wait takes every load (the last steps, which load nothing).
   auto step = [&](int t, int st, auto loads) {
     constexpr bool kLoads = decltype(loads)::value;
-    // Slab t + 2's resources are formed here, among slab t's matrix
+    // Slab t + S's resources are formed here, among slab t's matrix
     // instructions, rather than between the barrier and the loads.
-    const int k2 = (t + 2) * BK;
+    const int kn = (t + S) * BK;
     __amdgpu_buffer_rsrc_t qa = qz, qb = qz;
     if constexpr (kLoads) {
-      qa = rsrc_a(k2);
-      qb = rsrc_b(k2);
+      qa = rsrc_a(kn);
+      qb = rsrc_b(kn);
     }
     chunks(st);
     // Matrix instructions touch no memory, so the barrier alone does not
@@ -369,8 +383,8 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     // across the barrier and the wave still reaches it, and its next loads,
     // early.  With one group the compiler's own placement measured best.
     if constexpr (KS == 2) __builtin_amdgcn_sched_barrier(0);
-    const int nst = st ^ 1;
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+    const int nst = (t + 1) % S;
+    __builtin_amdgcn_s_waitcnt(VmWait<kLoads ? (S - 2) * Cfg::LOADS : 0>::imm);
     if (k_tail && t + 2 == nslab) fix_tail(t + 1, nst);
     __builtin_amdgcn_s_waitcnt(kLdsWait);
     asm volatile("s_barrier" ::: "memory");
@@ -388,20 +402,33 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
     }
   };
   if (nslab > 0) {
+    // Prologue: slabs 0 .. S - 2 go out at once, into stages 0 .. S - 2;
+    // slab 0 is waited for (with every slab behind it, when fewer than
+    // S - 2 follow), published, and slab S - 1 goes out.
     issue(rsrc_a(0), rsrc_b(0), 0);
-    __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
+#pragma unroll
+    for (int j = 1; j + 1 < S; ++j)
+      if (j < nslab) issue(rsrc_a(j * BK), rsrc_b(j * BK), j);
+    if (S == 2 || nslab >= S - 1)
+      __builtin_amdgcn_s_waitcnt(VmWait<(S - 2) * Cfg::LOADS>::imm);
+    else
+      __builtin_amdgcn_s_waitcnt(VmWait<0>::imm);
     if (k_tail && nslab == 1) fix_tail(0, 0);
     __builtin_amdgcn_s_waitcnt(kLdsWait);
     asm volatile("s_barrier" ::: "memory");
-    if (nslab > 1) issue(rsrc_a(BK), rsrc_b(BK), 1);
+    if (nslab > S - 1) issue(rsrc_a((S - 1) * BK), rsrc_b((S - 1) * BK), S - 1);
     read_chunk(fr[0], 0, 0);
     int t = 0;
-    for (; t + 2 < nslab; ++t) step(t, t & 1, std::true_type());
-    if (t + 1 < nslab) {
-      step(t, t & 1, std::false_type());
-      ++t;
+    for (; t + S < nslab; ++t) step(t, t % S, std::true_type());
+    if constexpr (S == 2) {
+      if (t + 1 < nslab) {
+        step(t, t % S, std::false_type());
+        ++t;
+      }
+    } else {
+      for (; t + 1 < nslab; ++t) step(t, t % S, std::false_type());
     }
-    chunks(t & 1);
+    chunks(t % S);
     mfma_chunk(fr[1], std::false_type(), qz, qz, 0, std::false_type());
   }
 

@@ -130,6 +130,7 @@ bool vec_b_ok(const float* B, int64_t ldb, int64_t N) {
 struct Variant {
   const char* name;
   int tile_m, tile_n, tile_k, threads, lds_bytes;
+  int stages;               // LDS slab buffers (STAGES - 1 slabs in flight)
   KernelFn vv, sv, vs, ss;  // by (A 128-bit?, B 128-bit?); null: unsupported
   KernelFn split;           // the split-K-across-workgroups form, or null
 };
@@ -137,7 +138,7 @@ struct Variant {
 template <int BM, int BN, int WM, int WN, int BK>
 Variant reg_variant(const char* name) {
   using Cfg = sg::MfmaCfg<BM, BN, WM, WN, BK>;
-  return {name, BM, BN, BK, Cfg::NT, Cfg::LDS_FLOATS * 4,
+  return {name, BM, BN, BK, Cfg::NT, Cfg::LDS_FLOATS * 4, 2,
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, true, true>,
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, false, true>,
           sg::sgemm_mfma_kernel<BM, BN, WM, WN, BK, true, false>,
@@ -146,12 +147,12 @@ Variant reg_variant(const char* name) {
 
 // The LDS-direct kernel takes rows of any 4-byte alignment, so one kernel
 // serves every load form.
-template <int BM, int BN, int WM, int WN, int BK, int KS>
+template <int BM, int BN, int WM, int WN, int BK, int KS, int ST = 2>
 Variant direct_variant(const char* name) {
-  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, KS>;
-  const KernelFn f = sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, KS>;
-  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, f, f, f, f,
-          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, KS, true>};
+  using Cfg = sg::DirectCfg<BM, BN, WM, WN, BK, KS, ST>;
+  const KernelFn f = sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, KS, ST>;
+  return {name, BM, BN, Cfg::BK, Cfg::NT, Cfg::LDS_FLOATS * 4, ST, f, f, f, f,
+          sg::sgemm_mfma_direct_kernel<BM, BN, WM, WN, BK, KS, ST, true>};
 }
 
 // Matrix-core configurations, large to small tiles, with the planner's two
