@@ -571,7 +571,8 @@ def main() -> int:
     if args.what in ("transpose", "all"):
         done += profile_transpose(raw, dest)
     if args.what in ("kscan", "all"):
-        for w in [args.workload] if args.workload and args.what == "kscan" else ["ragged"]:
+        for w in [args.workload] if args.workload and args.what == "kscan" else ["ragged",
+                                                                               "skinny"]:
             done += profile_kscan(w, raw, dest)
     say(f"{len(done)} summaries written")
     return 0
