@@ -415,6 +415,7 @@ def bench_ws(args) -> int:
                    "splits": plan.splits, "workspace_bytes": plan.workspace_bytes,
                    "workgroups": plan.workgroups, "threads": plan.threads,
                    "device": torch.cuda.get_device_name(dev),
+                   "source_hash": kernel_source_hash(),
                    "event_timed_launches": len(ev_ms),
                    "call_ms_median": round(float(np.median(ev_ms)), 5),
                    "sgemm_same_shape_tflops": round(flops * args.steps / wall_p / 1e12, 3),
