@@ -83,6 +83,9 @@ WORKLOADS = {
     # under-filled grids with a long K, for --op sgemm_ws (split K)
     "256x256x8192": (256, 256, 8192, "uniform", 6),
     "512x512x16384": (512, 512, 16384, "normal", 7),
+    "1024x1024x8192": (1024, 1024, 8192, "uniform", 8),
+    # one GPU's share of 4096^3 sharded eight ways along M
+    "512x4096x4096": (512, 4096, 4096, "uniform", 9),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.txt")
 

@@ -48,7 +48,7 @@ LDS_COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ
                 "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "GRBM_GUI_ACTIVE"]
 GEMM_WORKLOADS = ["4096cube", "8192cube", "skinny", "ragged", "256cube"]
-SPLIT_WORKLOADS = ["256x256x8192", "512x512x16384"]
+SPLIT_WORKLOADS = ["256x256x8192", "512x512x16384", "1024x1024x8192", "512x4096x4096"]
 TRANSPOSE_LAYOUTS = ["naive", "padded", "swizzled"]
 # kernel function names (as rocprofv3 -T prints them) of each plan family
 FAMILY_KERNEL = [("mfma_lds_", "sgemm_mfma_direct_kernel"), ("mfma_", "sgemm_mfma_kernel"),
@@ -290,6 +290,24 @@ def profile_gemm(workload: str, raw: str, dest: str) -> list:
     return written
 
 
+def _split_roles(rows: list, ts_key: str) -> tuple:
+    """Classify the product-kernel rows of an --op sgemm_ws run, given in
+    dispatch order: a partial-product dispatch is one directly followed by
+    the reduce kernel; plain sgemm's dispatches all follow the last reduce.
+    Returns (split rows, plain rows, reduce rows)."""
+    split, plain, red = [], [], []
+    last_red = max((i for i, r in enumerate(rows) if REDUCE_KERNEL in r["Kernel_Name"]),
+                   default=-1)
+    for i, r in enumerate(rows):
+        if REDUCE_KERNEL in r["Kernel_Name"]:
+            red.append(r)
+        elif i > last_red:
+            plain.append(r)
+        elif i + 1 < len(rows) and REDUCE_KERNEL in rows[i + 1]["Kernel_Name"]:
+            split.append(r)
+    return split, plain, red
+
+
 def profile_split(workload: str, raw: str, dest: str) -> list:
     made = header_cmd(f"split --workload {workload}")
     args = ["--op", "sgemm_ws", "--workload", workload]
@@ -301,37 +319,40 @@ def profile_split(workload: str, raw: str, dest: str) -> list:
     flops = 2.0 * M * N * K
     fn = "sgemm_mfma_direct_kernel"
     steps = b["steps"]
-    # The split kernel and plain sgemm share the kernel's name; their grids
-    # tell them apart (the split grid is S times the plain one).
-    split_grid = cfg["workgroups"] * cfg["threads"]
-    split_part = durations(out, fn, split_grid)[-steps:]
-    rows = [r for r in read_csv(out, "kernel_trace") if r["Kernel_Name"].startswith(fn)
-            and int(r["Grid_Size_X"]) != split_grid]
+    rows = [r for r in read_csv(out, "kernel_trace")
+            if r["Kernel_Name"].startswith(fn) or REDUCE_KERNEL in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    plain = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows][-steps:]
-    plain_grid = int(rows[-1]["Grid_Size_X"])
-    plain_wgs = plain_grid // int(rows[-1]["Workgroup_Size_X"])
-    red_t = durations(out, REDUCE_KERNEL)[-steps:]
+    sp_rows, pl_rows, rd_rows = _split_roles(rows, "Start_Timestamp")
+    dur = lambda rs: [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs]
+    split_part, plain, red_t = dur(sp_rows)[-steps:], dur(pl_rows)[-steps:], dur(rd_rows)[-steps:]
+    plain_wgs = int(pl_rows[-1]["Grid_Size_X"]) // int(pl_rows[-1]["Workgroup_Size_X"])
     avg = lambda xs: sum(xs) / len(xs)
     short = args + ["--steps", "5", "--warmup", "1", "--warmup-seconds", "0"]
     fs, ws, _ = copy_scale(raw)
-    res_s, cmds = traffic_pass(raw, f"traffic_ws_{workload}", short, split_grid)
-    res_p, _ = traffic_pass(raw, f"traffic_ws_plain_{workload}", short, plain_grid)
-    res_r, _ = traffic_pass(raw, f"traffic_ws_reduce_{workload}", short)
+    per, cmds = {}, []
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        outc, _, cmd = rocprof(raw, f"traffic_ws_{workload}_{c}", ["--pmc", c], short, 180)
+        cmds.append(cmd)
+        crow = [r for r in read_csv(outc, "counter_collection") if r["Counter_Name"] == c and
+                (r["Kernel_Name"].startswith(fn) or REDUCE_KERNEL in r["Kernel_Name"])]
+        crow.sort(key=lambda r: int(r["Dispatch_Id"]))
+        for role, rs in zip(("split", "plain", "reduce"), _split_roles(crow, "Dispatch_Id")):
+            vals = [float(r["Counter_Value"]) for r in rs]
+            per.setdefault(role, {})[c] = sum(vals) / len(vals)
 
-    def hbm(res, kernel):
-        f, w = kib(res, kernel, "FETCH_SIZE")[0], kib(res, kernel, "WRITE_SIZE")[0]
+    def hbm(role):
+        f, w = per[role]["FETCH_SIZE"], per[role]["WRITE_SIZE"]
         return (f * fs + w * ws) * 1024, f, w
 
-    hs, hp, hr = hbm(res_s, fn), hbm(res_p, fn), hbm(res_r, REDUCE_KERNEL)
+    hs, hp, hr = hbm("split"), hbm("plain"), hbm("reduce")
     call = avg(split_part) + avg(red_t)
     lines = [f"# K split across workgroups (sgemm_ws): {cfg['kernel']}, M={M} N={N} K={K}, "
              f"{S} splits", made,
              f"command_trace: {cmd_t}",
              f"command_counters: {cmds[0]}   (then WRITE_SIZE, each in a run of its own; "
              f"scale factors from the 256 MiB copy calibration: fetch {fs:.4f}, write "
-             f"{ws:.4f}); the split kernel's dispatches ({split_grid} work-items) and plain "
-             f"sgemm's ({plain_grid}) are told apart by their grids",
+             f"{ws:.4f}); a partial-product dispatch is the one followed by the sum kernel, "
+             f"plain sgemm's follow the last sum",
              f"device: {cfg.get('device')}, 1 GPU; source_hash: {cfg.get('source_hash')}", "",
              f"per kernel, trace average over the {steps} timed dispatches:",
              f"  partial products (split kernel): {fn}, {cfg['workgroups']} workgroups",
