@@ -204,8 +204,12 @@ int sgemm_ws(int64_t M, int64_t N, int64_t K,
  * that device's one scratch, which keeps the last call's partials (each
  * split call overwrites all it reads): calls that overlap on one device (on
  * different streams, or from different threads without ordering) race and
- * must not be made.  Other arguments, checks and return codes are sgemm_ws's;
- * SGEMM_ERR_LAUNCH also when the scratch's address cannot be had. */
+ * must not be made.  Under HIP graph capture, make one split call on the
+ * device before capturing, so that the address lookup (a HIP runtime query,
+ * not a stream operation) is not made inside the capture; the captured
+ * launches then read and write the scratch at replay, in stream order.
+ * Other arguments, checks and return codes are sgemm_ws's; SGEMM_ERR_LAUNCH
+ * also when the scratch's address cannot be had. */
 int sgemm_ws_noalloc(int64_t M, int64_t N, int64_t K,
                      const float *A, int64_t lda,
                      const float *B, int64_t ldb,

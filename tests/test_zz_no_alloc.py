@@ -72,3 +72,69 @@ def test_no_alloc_matches_sgemm_ws_on_two_calls():
         err = assert_close(got[rows], Cref, T, f"sgemm_ws_noalloc {M}x{N}x{K}")
         say(f"  bit-equal to sgemm_ws; max normalised error {err:.2e}")
         del ws
+
+
+@pytest.mark.gpu
+def test_no_alloc_replays_under_graph_capture():
+    """Captured in a HIP graph after one eager call (which makes the scratch
+    lookup), the split product replays to the eager bits; eager calls of
+    another shape between the replays overwrite the shared scratch, which
+    each replay rewrites before it reads."""
+    import torch
+
+    from gpu_util import say
+    dev = torch.device("cuda:0")
+    M, N, K = 256, 256, 8192
+    A, B = seedgen.gemm_inputs(M, N, K, "uniform", 73)
+    tA, tB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    need = sg.sgemm_workspace_bytes(M, N, K)
+    assert 0 < need <= sg.NOALLOC_MAX_BYTES
+    C = torch.empty((M, N), device=dev)
+    M2, N2, K2 = 200, 300, 10001
+    A2, B2 = seedgen.gemm_inputs(M2, N2, K2, "uniform", 74)
+    tA2, tB2 = torch.from_numpy(A2).to(dev), torch.from_numpy(B2).to(dev)
+    need2 = sg.sgemm_workspace_bytes(M2, N2, K2)
+    assert 0 < need2 <= sg.NOALLOC_MAX_BYTES
+    C2 = torch.empty((M2, N2), device=dev)
+
+    def call():
+        s = torch.cuda.current_stream().cuda_stream
+        return sg.sgemm_ws_noalloc(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N,
+                                   C.data_ptr(), N, s, need)
+
+    def other():
+        s = torch.cuda.current_stream().cuda_stream
+        return sg.sgemm_ws_noalloc(M2, N2, K2, tA2.data_ptr(), K2, tB2.data_ptr(), N2,
+                                   C2.data_ptr(), N2, s, need2)
+
+    say(f"[gpu] sgemm_ws_noalloc graph: eager {M}x{N}x{K}")
+    assert call() == sg.OK
+    torch.cuda.synchronize()
+    want = C.clone()
+    assert other() == sg.OK
+    torch.cuda.synchronize()
+    want2 = C2.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm up on the capture stream
+        assert call() == sg.OK
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    say("[gpu] sgemm_ws_noalloc graph: capture")
+    with torch.cuda.graph(graph):
+        assert call() == sg.OK
+    for rep in range(4):
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"[gpu] sgemm_ws_noalloc graph: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, want), rep
+        # eager work between the replays: another split call through the scratch
+        C2.fill_(float("nan"))
+        assert other() == sg.OK
+        torch.cuda.synchronize()
+        assert torch.equal(C2, want2), rep
