@@ -138,3 +138,23 @@ def test_ladder_register_tiles_cut_lds_reads(asm, tm, layout):
     fmas = len(re.findall(r"^\s+v_fmac?_f32(?:_e32|_e64)?\s", body, re.M))
     assert fmas > 0
     assert words / fmas == pytest.approx((tm + tm) / (tm * tm)), (words, fmas)
+
+
+@pytest.mark.parametrize("frag,ta,tb,subs", DIRECT, ids=[d[0] for d in DIRECT])
+def test_direct_kernel_c_stores(asm, frag, ta, tb, subs):
+    """The epilogue's stores: with one 32-column block per wave, one 32-bit
+    store per accumulator element (TA blocks of 16 per lane); with two, whose
+    columns interleave, one 64-bit store per pair of elements, and in the
+    separate path of a tile on C's right edge one 32-bit store per element.
+    A product's C goes out with the nontemporal hint, the split partials,
+    which the reduction reads straight back, without it."""
+    want = ({"buffer_store_dword": ta * 16} if tb == 1 else
+            {"buffer_store_dwordx2": ta * 16, "buffer_store_dword": 2 * ta * 16})
+    for split, hint in (("Lb0E", True), ("Lb1E", False)):
+        body = kernel_body(asm, "sgemm_mfma_direct_kernel", frag + "Li2E" + split)
+        stores = re.findall(r"^\s+(buffer_store\S*)\s+([^\n]*)$", body, re.M)
+        got = {}
+        for op, _ in stores:
+            got[op] = got.get(op, 0) + 1
+        assert got == want, split
+        assert all(ops.rstrip().endswith(" nt") == hint for _, ops in stores), split

@@ -285,6 +285,12 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   // successor's loads any later costs more than the burst does.
   constexpr bool kSpread = KS == 1;
 
+  // With two 32-column blocks per wave, block j takes the wave's columns
+  // 2 li + j rather than 32 j + li: a lane's two B words of a k step are
+  // then adjacent (one 64-bit LDS read) and so are its two C words of a row
+  // (one 64-bit store).
+  constexpr bool kPairB = TB == 2;
+
   // The chunk pipeline described at the top of the file.
   constexpr int NCH = 2 * SUB_G;  // chunks per slab of this wave group
   struct Frag {
@@ -307,11 +313,20 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const int k = 16 * sub + 8 * lh + 4 * h + pp;
-#pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        const int col = wn0 + 32 * j + li;
+      if constexpr (kPairB) {
+        // Columns 2 li and 2 li + 1 of the wave's 64: one 64-bit read.
+        const int col = wn0 + 2 * li;
         const int q = (col >> 2) ^ (lh ? 8 : 0);
-        f.b[j][pp] = bs[4 * (k * QB + q) + (col & 3)];
+        const f32x2 v = *reinterpret_cast<const f32x2*>(bs + 4 * (k * QB + q) + (col & 3));
+        f.b[0][pp] = v[0];
+        f.b[1][pp] = v[1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < TB; ++j) {
+          const int col = wn0 + 32 * j + li;
+          const int q = (col >> 2) ^ (lh ? 8 : 0);
+          f.b[j][pp] = bs[4 * (k * QB + q) + (col & 3)];
+        }
       }
     }
   };
@@ -468,6 +483,47 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
   int ln = lane;
   asm volatile("" : "+v"(ln));
   const int li_c = ln & 31, lh_c = ln >> 5;
+  if constexpr (kPairB) {
+    const int col = wn0 + 2 * li_c;   // and col + 1, from the tile's corner
+    // Inside C's columns the pair goes out as one 64-bit store; at the
+    // tile's right edge each word is stored (or dropped) on its own.
+    const bool edge = n_left < wn0 + WN;
+    const bool ok0 = col < n_left, ok1 = col + 1 < n_left;
+    auto store_rows = [&](auto at_edge) {
+#pragma unroll
+      for (int i = 0; i < TA; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * lh_c + (r & 3);
+          const uint32_t at = ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u;
+          const bool row_ok = row < m_left;
+          if constexpr (decltype(at_edge)::value) {
+            const uint32_t off0 = row_ok && ok0 ? at : kOob;
+            const uint32_t off1 = row_ok && ok1 ? at + 4u : kOob;
+            if constexpr (SPLIT) {
+              store1(rc, off0, acc[i][0][r]);
+              store1(rc, off1, acc[i][1][r]);
+            } else {
+              store1_nt(rc, off0, acc[i][0][r]);
+              store1_nt(rc, off1, acc[i][1][r]);
+            }
+          } else {
+            const f32x2 v = {acc[i][0][r], acc[i][1][r]};
+            const uint32_t off = row_ok ? at : kOob;
+            if constexpr (SPLIT)
+              store2(rc, off, v);
+            else
+              store2_nt(rc, off, v);
+          }
+        }
+      }
+    };
+    if (edge)
+      store_rows(std::true_type());
+    else
+      store_rows(std::false_type());
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TA; ++i) {
 #pragma unroll
@@ -478,8 +534,12 @@ sgemm_mfma_direct_kernel(GemmArgs g_in) {
       for (int r = 0; r < 16; ++r) {
         const int row = wm0 + 32 * i + 8 * (r >> 2) + 4 * lh_c + (r & 3);
         const bool ok = col_ok && row < m_left;
-        store1(rc, ok ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob,
-               acc[i][j][r]);
+        const uint32_t off =
+            ok ? ((uint32_t)row * (uint32_t)g.ldc + (uint32_t)col) * 4u : kOob;
+        if constexpr (SPLIT)
+          store1(rc, off, acc[i][j][r]);
+        else
+          store1_nt(rc, off, acc[i][j][r]);
       }
     }
   }
