@@ -101,7 +101,7 @@ def test_fma_kernel_is_the_8x8_register_tile(asm, flags):
 
 # (template fragment, TA, TB, 16-deep sub-slabs per wave group per slab)
 DIRECT = [("Li256ELi256ELi64ELi64ELi32ELi1E", 2, 2, 2),
-          ("Li128ELi128ELi64ELi32ELi32ELi1E", 2, 1, 2),
+          ("Li128ELi128ELi32ELi64ELi32ELi1E", 1, 2, 2),
           ("Li64ELi128ELi32ELi64ELi32ELi1E", 1, 2, 2),
           ("Li64ELi128ELi32ELi64ELi32ELi2E", 1, 2, 1),
           ("Li64ELi64ELi32ELi32ELi32ELi1E", 1, 1, 2),

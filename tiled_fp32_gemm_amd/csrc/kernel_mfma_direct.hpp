@@ -46,12 +46,17 @@
 //     (16 consecutive rows, one k group) is 256 contiguous bytes.
 //   B stage (BK x BN): rows as in memory with the 16-byte units of rows whose
 //     bit 3 is set XOR-swizzled by 8: unit(k, q) = k BN/4 + (q ^ 8 [k & 8]).
-//     The 32-bit reads give lanes 0-31 row 16 s + p and lanes 32-63 row
+//     The B reads give lanes 0-31 row 16 s + p and lanes 32-63 row
 //     16 s + 8 + p of sub-slab s; the swizzle puts the two halves on the two
 //     disjoint halves of the banks (the pages' XOR swizzle idea,
 //     "Memory-bank mechanism and accelerated compute", section on
 //     alternatives to padding, applied at 16-byte granularity so that the
-//     128-bit units stay whole).
+//     128-bit units stay whole).  With one 32-column block per wave a lane
+//     reads one word per row; with two, block j takes the wave's columns
+//     2 i + j (i = lane mod 32) instead of 32 j + i, so a lane's two words
+//     of a row are adjacent and come in one 64-bit read (32 lanes: 256
+//     contiguous bytes), and its two C values of a row leave in one 64-bit
+//     store.
 //
 // Pipeline.  Slabs rotate through STAGES LDS stages (two for the large tiles,
 // whose stages fill the LDS; four for small tiles, whose slabs compute too

@@ -185,7 +185,7 @@ const Candidate* mfma_candidates(bool direct, int& n) {
   // number of wave groups that split each slab.
   static const Candidate lds[8] = {
       {direct_variant<256, 256, 64, 64, 32, 1>("mfma_lds_256x256x32"), 0.929, 1},
-      {direct_variant<128, 128, 64, 32, 32, 1>("mfma_lds_128x128x32"), 0.895, 2},
+      {direct_variant<128, 128, 32, 64, 32, 1>("mfma_lds_128x128x32"), 0.895, 2},
       {direct_variant<64, 128, 32, 64, 32, 1>("mfma_lds_64x128x32"), 0.901, 3},
       {direct_variant<64, 128, 32, 64, 32, 2>("mfma_lds_64x128x32_ks2"), 0.805, 3},
       {direct_variant<64, 64, 32, 32, 32, 1>("mfma_lds_64x64x32"), 0.837, 5},
