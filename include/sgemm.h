@@ -193,7 +193,8 @@ int sgemm_ws(int64_t M, int64_t N, int64_t K,
  * workspace is a file-scope device array of SGEMM_NOALLOC_MAX_BYTES that the
  * library holds on each device it runs on until the process ends (its
  * address is looked up once per device, on the first call that splits K on
- * it); the call itself allocates nothing and frees nothing.
+ * it; the device is the stream's, or the current one for the null stream);
+ * the call itself allocates nothing and frees nothing.
  *   workspace_bytes  the room the plan may take from the scratch, as
  *                    sgemm_ws's workspace_bytes (0 allows no split), at most
  *                    SGEMM_NOALLOC_MAX_BYTES; more is SGEMM_ERR_SCRATCH_LIMIT

@@ -487,16 +487,31 @@ struct ScratchSlot {
 ScratchSlot g_scratch[kMaxDevices];
 
 // The device address of device dev's scratch, looked up once per device
-// (dev must be the current device); null when HIP reports an error.
+// with dev current (made current for the lookup when it is not, and the
+// caller's device restored); null when HIP reports an error.
 float* scratch_of(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return nullptr;
   ScratchSlot& slot = g_scratch[dev];
-  std::call_once(slot.once, [&slot] {
+  std::call_once(slot.once, [&slot, dev] {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return;
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
       slot.ptr = static_cast<float*>(p);
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) slot.ptr = nullptr;
   });
   return slot.ptr;
+}
+
+// The device a launch on stream runs on: the stream's own, or for the null
+// stream the current device.
+bool stream_device(hipStream_t stream, int& dev) {
+  if (stream == nullptr) return hipGetDevice(&dev) == hipSuccess;
+  hipDevice_t d = -1;
+  if (hipStreamGetDevice(stream, &d) != hipSuccess) return false;
+  dev = (int)d;
+  return true;
 }
 
 // The ablation ladder.  Each step changes one thing against the one before;
@@ -629,7 +644,7 @@ int sgemm_ws_noalloc(int64_t M, int64_t N, int64_t K, const float* A, int64_t ld
     return launch_gemm(p.fn, M, N, K, A, lda, B, ldb, C, ldc, c, p.info.tile_m,
                        p.info.tile_n, p.info.threads, stream);
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return SGEMM_ERR_LAUNCH;
+  if (!stream_device(stream, dev)) return SGEMM_ERR_LAUNCH;
   float* const W = scratch_of(dev);
   if (W == nullptr) return SGEMM_ERR_LAUNCH;
   const int64_t wb = p.info.workspace_bytes;
