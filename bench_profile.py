@@ -23,7 +23,8 @@ factor each counter reads on a plain 256 MiB device copy.
   python3 bench_profile.py all                        all of the above, every workload
 
 --out sets where the summaries go (default: profiles/ of this checkout),
---raw where rocprofv3 writes (default: gpurun_out/prof).  The pages ask for a
+--raw where rocprofv3 writes its raw output (default: sgemm_prof_raw under
+the system's temporary directory).  The pages ask for a
 fixed, repeatable measurement: warm up, repeat, keep the median and spread,
 read the bank-conflict counter, and check the result before comparing times
 ("Memory-bank mechanism and accelerated compute", section on turning
@@ -39,6 +40,7 @@ import json
 import os
 import subprocess
 import sys
+import tempfile
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -577,7 +579,7 @@ def main() -> int:
     ap.add_argument("what", choices=["gemm", "split", "ladder", "transpose", "kscan", "all"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
-    ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--raw", default=os.path.join(tempfile.gettempdir(), "sgemm_prof_raw"))
     args = ap.parse_args()
     raw, dest = os.path.abspath(args.raw), os.path.abspath(args.out)
     done = []
