@@ -334,6 +334,43 @@ def test_every_direct_variant_one_to_three_slabs(kernel, M, N, K):
     assert np.all(np.isnan(C[:, N:])), "C padding written"
 
 
+# (kernel, M, N, K): tiles with two 32-column blocks per wave store C as
+# column pairs, and a tile on C's right edge takes its own path that stores
+# each word under its own mask.  N leaves an odd number of columns in the
+# last tile column (5 or 37), so a lane there holds one valid column of its
+# pair, and whole waves of the tile lie past N.  Integer data: every order
+# gives the same bits; C's padding columns must stay untouched.
+PAIR_EDGE_SHAPES = [
+    ("mfma_lds_256x256x32", 4096, 3845, 1200),
+    ("mfma_lds_256x256x32", 3840, 4133, 1000),
+    ("mfma_lds_128x128x32", 4096, 4101, 64),
+    ("mfma_lds_64x128x32", 4096, 4101, 256),
+]
+
+
+@pytest.mark.parametrize("kernel,M,N,K", PAIR_EDGE_SHAPES,
+                         ids=[f"{v[0]}-{v[1]}x{v[2]}x{v[3]}" for v in PAIR_EDGE_SHAPES])
+def test_paired_columns_at_the_right_edge(kernel, M, N, K):
+    import tiled_fp32_gemm_amd as sg
+    lda, ldc = K + 1, N + 2
+    A = np.full((M, lda), np.nan, np.float32)
+    A[:, :K] = seedgen.integer_matrix(M, K, -8, 8, 2300 + K)
+    B = seedgen.integer_matrix(K, N, -8, 8, 2300 + K, start=M * K)
+    dA, dB = DevMat(A), DevMat(B)
+    dC = DevMat(np.full((M, ldc), np.nan, np.float32))
+    st, plan = sg.sgemm_plan_query(M, N, K, dA.ptr, lda, dB.ptr, N, dC.ptr, ldc, 0)
+    assert st == sg.OK and plan.kernel.decode().rsplit("_", 1)[0] == kernel
+    say(f"[gpu] paired-column edge {kernel} M={M} N={N} K={K}")
+    st = sg.sgemm(M, N, K, dA.ptr, lda, dB.ptr, N, dC.ptr, ldc,
+                  torch.cuda.current_stream().cuda_stream)
+    assert st == sg.OK
+    torch.cuda.synchronize()
+    C = dC.host()
+    Cref, _ = oracle.gemm(A[:, :K], B, M=M, N=N, K=K, with_t=False)
+    assert np.array_equal(C[:, :N], Cref.astype(np.float32))
+    assert np.all(np.isnan(C[:, N:])), "C padding written"
+
+
 @pytest.mark.parametrize("kernel,M,N,K", VARIANT_SHAPES, ids=[v[0] for v in VARIANT_SHAPES])
 @pytest.mark.parametrize("odd_lda", [False, True])
 def test_every_direct_variant(kernel, M, N, K, odd_lda):

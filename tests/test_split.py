@@ -118,7 +118,10 @@ def test_split_within_tolerance(shape):
     assert ws.guards_intact(p.workspace_bytes), "workspace written out of range"
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 8192), (131, 97, 6001), (32, 4096, 4096)])
+# 512 x 645 x 16384 splits with 64 x 128 tiles, whose partial tiles leave the
+# kernel as column pairs: N = 645 ends five columns into the last tile.
+@pytest.mark.parametrize("M,N,K", [(256, 256, 8192), (131, 97, 6001), (32, 4096, 4096),
+                                   (512, 645, 16384)])
 def test_split_integer_data_bitexact(M, N, K):
     import tiled_fp32_gemm_amd as sg
     A = seedgen.integer_matrix(M, K, -8, 8, 40 + K)
