@@ -755,6 +755,14 @@ def main() -> int:
             "operand_sets": nsets,
             "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
             "compulsory_hbm_gbs": round(compulsory / kern_s / 1e9, 1),
+            "compulsory_pct_of_hbm_peak": round(100.0 * compulsory / kern_s / 1e9
+                                                / PEAK_HBM_GBS, 2),
+            # the counted HBM bytes (roofline.traffic) over the same time
+            "traffic_hbm_gbs": (round(traffic / kern_s / 1e9, 1)
+                                if traffic is not None else None),
+            "traffic_pct_of_hbm_peak": (round(100.0 * traffic / kern_s / 1e9
+                                              / PEAK_HBM_GBS, 2)
+                                        if traffic is not None else None),
             "event_timed_launches": len(ev_ms),
             "kernel_ms_median": round(float(np.median(ev_ms)), 5),
             "kernel_ms_p10_p90": [round(float(np.percentile(ev_ms, 10)), 5),

@@ -80,6 +80,14 @@ def test_gemm_line(capsys):
     # a matrix-core clock between 1 and 3 GHz, and versions recorded
     assert 1.0 < cfg["clock"]["mfma_clock_ghz"] < 3.0
     assert cfg["versions"]["hip_runtime"] > 0
+    # the HBM side of the roofline: compulsory bytes, and the counted bytes
+    # when profiles/ holds them for this kernel
+    assert 0 < cfg["compulsory_pct_of_hbm_peak"] < 100
+    tr = d["roofline"]["traffic"]
+    assert (cfg["traffic_hbm_gbs"] is None) == (tr is None)
+    if tr is not None:
+        assert cfg["traffic_pct_of_hbm_peak"] == pytest.approx(
+            100 * cfg["traffic_hbm_gbs"] / 8000, abs=0.02)
 
 
 @pytest.mark.gpu
