@@ -58,10 +58,10 @@
 //     contiguous bytes), and its two C values of a row leave in one 64-bit
 //     store.
 //
-// Pipeline.  Slabs rotate through STAGES LDS stages (two for the large tiles,
-// whose stages fill the LDS; four for small tiles, whose slabs compute too
-// briefly to cover a load's latency with one slab in flight), so that
-// STAGES - 1 slabs are in flight.  A wave reads its MFMA
+// Pipeline.  Slabs rotate through STAGES LDS stages, so that STAGES - 1
+// slabs are in flight.  Every variant the library launches uses two: on
+// MI355X three and four stages timed level or slower for the small tiles as
+// well, whose slabs compute briefly.  A wave reads its MFMA
 // fragments one 8-deep chunk ahead of the matrix instructions that use them,
 // into two register sets of one chunk each (the registers one 16-deep
 // sub-slab would take), and the slab barrier sits before the last chunk's
